@@ -1,0 +1,324 @@
+"""Benchmark of the ViT vision-tower forward on one MI355X.
+
+One step = one whole forward of the 27-block tower with its four mergers
+(patch embed, 27 x [LN-quant, QKV FP8 GEMM, RoPE, attention, quant, proj,
+LN-quant, FC1 (+GELU, requant), FC2], 4 x [merge + LN, fc1 + GELU, fc2]) on
+one synthetic image of 46 x 136 = 6256 patches, inputs resident in HBM.
+
+Prints ONE JSON line.  `value` is milliseconds per image (lower is better).
+The `roofline` object is the attention kernel (the tower's largest cost):
+algorithmic FLOPs per launch (4 * P^2 * 1152) over its average launch
+duration, measured here with HIP events on the stream it runs on, at the
+launch configuration the tower uses.  `kernels` gives the same for every
+kernel of the step.  `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the same workload (one block, the patch embed and one merger at
+6256 patches) and scales it to the whole forward.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload encoder_p6256]
+                       [--no-cpu-baseline] [--kernels/--no-kernels]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+METRIC = "ViT fwd ms/image @6256 patches; attention TFLOP/s as % of MI355X bf16 MFMA peak"
+
+WORKLOADS = {
+    "encoder_p6256": dict(grids=[(46, 136)], cfg=3,
+                          desc="27-block ViT tower + 4 mergers, 1 image of 46x136 = 6256 patches"),
+    "encoder_varlen_6684": dict(grids=[(18, 54), (36, 108), (24, 76)], cfg=4,
+                                desc="27-block ViT tower + 4 mergers, 3 packed images of 972 + 3888 + 1824 patches"),
+    "encoder_p3888": dict(grids=[(36, 108)], cfg=3, desc="27-block ViT tower + 4 mergers, 1 image of 3888 patches"),
+    "encoder_p1824": dict(grids=[(24, 76)], cfg=3, desc="27-block ViT tower + 4 mergers, 1 image of 1824 patches"),
+    "encoder_p972": dict(grids=[(18, 54)], cfg=3, desc="27-block ViT tower + 4 mergers, 1 image of 972 patches"),
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "vision_transformer_encoder_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def encoder_flops(seq_lens, depth=27, n_mergers=4):
+    """Algorithmic FLOPs of one forward (2 per multiply-add; no padding)."""
+    H, MLP, PD, MD, OUT = 1152, 4304, 1536, 4608, 4096
+    T = sum(seq_lens)
+    d = dict(attention=depth * sum(4 * p * p * H for p in seq_lens),
+             gemm=depth * 2 * T * H * (3 * H + H + MLP + MLP),
+             patch=2 * T * PD * H, mergers=n_mergers * 2 * (T // 4) * MD * (MD + OUT))
+    d["total"] = sum(d.values())
+    return d
+
+
+def cpu_baseline(grids, cfg):
+    """Time the fp64 oracle on one block, the patch embed and one merger of
+    the workload and scale to the whole forward (27 blocks, 4 mergers)."""
+    import numpy as np
+    import oracle as O
+    import synth
+    from oracle import inputs as OI
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    T = sum(h * w for h, w in grids)
+    pos, cu = O.positions_from_grids(grids), O.cu_seqlens_from_grids(grids)
+    bw = OI.block_weights(synth.block_params(cfg, 0))
+    for n in ("qkv", "proj", "fc1", "fc2"):
+        bw.fp8(n)  # weight preparation is not part of a forward
+    mw = OI.merger_weights(synth.merger_params(cfg, 0))
+    pp = synth.patch_params(cfg)
+    ew = O.EncoderWeights(patch_w=OI.dec(pp["patch_w"]), patch_b=OI.dec(pp["patch_b"]), blocks=[], mergers=[])
+    px = synth.pixels(cfg, T).astype(np.float64)
+    t0 = time.perf_counter()
+    x = O.patch_embed(px, ew)
+    t1 = time.perf_counter()
+    x = O.block_forward(x, bw, pos, cu)
+    t2 = time.perf_counter()
+    O.merger_forward(x, mw, grids)
+    t3 = time.perf_counter()
+    est_s = (t1 - t0) + 27 * (t2 - t1) + 4 * (t3 - t2)
+    return {"value": est_s * 1e3 / len(grids), "unit": "ms/image", "cores": int(threads), "kind": "oracle",
+            "sample": f"patch embed + 1 of 27 blocks + 1 of 4 mergers at {T} patches "
+                      f"({t3 - t0:.1f} s measured: patch {t1 - t0:.2f} s, block {t2 - t1:.2f} s, "
+                      f"merger {t3 - t2:.2f} s), scaled to 27 blocks + 4 mergers",
+            "measured_s": round(t3 - t0, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="encoder_p6256", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel event timings")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the tower shards by image with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import vision_transformer_encoder_amd as vit
+
+    vit.require_library()
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+    grids, cfg = wl["grids"], wl["cfg"]
+    T = sum(h * w for h, w in grids)
+    nimg = len(grids)
+
+    print(f"[bench] workload {args.workload}: T={T}, images={nimg}", file=sys.stderr, flush=True)
+    ep = synth.encoder_params(cfg)
+    W = vit.EncoderWeights(ep.patch, ep.blocks, ep.mergers, dev)
+    px = torch.from_numpy(synth.pixels(cfg, T)).to(dev)
+    g_host = np.asarray(grids, dtype=np.int32).reshape(-1, 2)
+    g_dev = torch.from_numpy(g_host.copy()).to(dev)
+    ws = torch.empty(vit.vit_encoder_workspace_size(T, nimg), dtype=torch.uint8, device=dev)
+    out = torch.empty((4, T // 4, 4096), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    print("[bench] weights ready", file=sys.stderr, flush=True)
+
+    def step():
+        vit.vit_encoder_forward(W, px, grids, workspace=ws, out=out, grid_dev=g_dev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
+          file=sys.stderr, flush=True)
+    ok = bool(torch.isfinite(out.float()).all().item())
+
+    flops = encoder_flops([h * w for h, w in grids])
+    seq = [h * w for h, w in grids]
+    kernels = {}
+    roofline = None
+    if not args.no_kernels:
+        kernels = time_kernels(vit, W, T, grids, dev, args.kernel_reps, seq)
+        a = kernels["attention"]
+        roofline = {"bound": "mfma", "achieved": a["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(a["tflops"] / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic_from_profiles("attention"),
+                    "kernel": "attention_kernel", "avg_launch_us": a["us"],
+                    "algorithmic_flop_per_launch": a["flop"]}
+
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_step / nimg, 4),
+        "unit": "ms/image",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 GEMMs + bf16 attention, fp32 accumulate",
+        "data": "synthetic (seeded; random-init weights of the tower's shapes)",
+        "config": {"workload": args.workload, "description": wl["desc"], "patches": T, "images": nimg,
+                   "grids": grids, "blocks": 27, "mergers": 4},
+        "throughput": {"tflops_total": round(flops["total"] / (ms_per_step * 1e-3) / 1e12, 1),
+                       "algorithmic_gflop_per_step": round(flops["total"] / 1e9, 1),
+                       "images_per_s": round(1e3 * nimg / ms_per_step, 2)},
+        "outputs_finite": ok,
+    }
+    if roofline is not None:
+        line["roofline"] = roofline
+        line["kernels"] = kernels
+        per_step = {k: v["us"] * v["per_step"] for k, v in kernels.items()}
+        line["kernel_time_share"] = {k: round(v / (ms_per_step * 1e3), 3) for k, v in per_step.items()}
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(grids, cfg)
+    print(json.dumps(line), flush=True)
+    return 0 if ok else 1
+
+
+def time_kernels(vit, W, T, grids, dev, reps, seq):
+    """Average launch duration of each kernel of the step, at the shapes and
+    launch configuration the tower uses, measured with HIP events on the
+    current stream (the stream every launch goes to)."""
+    import numpy as np
+    import torch
+
+    H = 1152
+    b0 = W.blocks[0]
+    t = b0.t
+    q = b0.q
+    x = torch.randn((T, H), device=dev).to(torch.bfloat16)
+    pos = torch.from_numpy(np.concatenate([np.stack(np.meshgrid(np.arange(h), np.arange(w), indexing="ij"), -1)
+                                           .reshape(-1, 2) for h, w in grids]).astype(np.int32)).to(dev)
+    cu = np.concatenate([[0], np.cumsum([h * w for h, w in grids])]).astype(np.int32)
+    cu_dev = torch.from_numpy(cu).to(dev)
+    g_dev = torch.from_numpy(np.asarray(grids, np.int32).reshape(-1, 2)).to(dev)
+    qkv = torch.randn((T, 3 * H), device=dev).to(torch.bfloat16)
+    a_c, a_s = vit.vit_layernorm_quant_fp8(x, t["ln1_g"], t["ln1_b"])
+    h_c, h_s = vit.vit_fp8_block128_gemm(a_c, a_s, q["fc1"][0], q["fc1"][1], 4304, 1152, bias=t["fc1_b"],
+                                         epilogue=vit.EPI_BIAS_GELU_FP8)
+    o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    xr = x.clone()
+    m = W.mergers[0].t
+    TM = T // 4
+    mln = torch.randn((TM, 4608), device=dev).to(torch.bfloat16)
+    mh = torch.empty((TM, 4608), dtype=torch.bfloat16, device=dev)
+    mo = torch.empty((TM, 4096), dtype=torch.bfloat16, device=dev)
+    px = torch.rand((T, 1536), device=dev) * 2 - 1
+    xp = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    att_flop = sum(4 * p * p * H for p in seq)
+    gemm = lambda n, k: 2 * T * n * k
+    B = 27
+    cases = {
+        # name: (callable, work, unit, per_step)
+        "layernorm_quant": (lambda: vit.vit_layernorm_quant_fp8(x, t["ln1_g"], t["ln1_b"]),
+                            T * (H * 2 + H + 9 * 4), "B", 2 * B),
+        "fp8_gemm_qkv": (lambda: vit.vit_fp8_block128_gemm(a_c, a_s, q["qkv"][0], q["qkv"][1], 3 * H, H,
+                                                           bias=t["qkv_b"], out=qkv), gemm(3 * H, H), "F8", B),
+        "rope2d": (lambda: vit.vit_rope2d(qkv[:, :H], qkv[:, H:2 * H], pos), T * 2 * H * 2 * 2 + T * 8, "B", B),
+        "attention": (lambda: vit.vit_attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], cu, cu_seqlens_dev=cu_dev,
+                                                out=o), att_flop, "F16", B),
+        "quant_rows": (lambda: vit.vit_quant_fp8_block128(o), T * (H * 2 + H + 9 * 4), "B", B),
+        "fp8_gemm_proj": (lambda: vit.vit_fp8_block128_gemm(a_c, a_s, q["proj"][0], q["proj"][1], H, H,
+                                                            bias=t["proj_b"], residual=xr,
+                                                            epilogue=vit.EPI_BIAS_RESIDUAL, out=xr),
+                          gemm(H, H), "F8", B),
+        "fp8_gemm_fc1_gelu_quant": (lambda: vit.vit_fp8_block128_gemm(a_c, a_s, q["fc1"][0], q["fc1"][1], 4304, H,
+                                                                      bias=t["fc1_b"],
+                                                                      epilogue=vit.EPI_BIAS_GELU_FP8),
+                                    gemm(4304, H), "F8", B),
+        "fp8_gemm_fc2": (lambda: vit.vit_fp8_block128_gemm(h_c, h_s, q["fc2"][0], q["fc2"][1], H, 4304,
+                                                           bias=t["fc2_b"], residual=xr,
+                                                           epilogue=vit.EPI_BIAS_RESIDUAL, out=xr),
+                         gemm(H, 4304), "F8", B),
+        "patch_embed_bf16": (lambda: vit.vit_bf16_gemm(px, W.patch["patch_w"], bias=W.patch["patch_b"], out=xp),
+                             gemm(H, 1536), "F16", 1),
+        "merge_layernorm": (lambda: vit.vit_merge2x2_layernorm(x, grids, m["m_ln_g"], m["m_ln_b"], grid_dev=g_dev),
+                            2 * T * H * 2, "B", 4),
+        "merger_fc1_bf16": (lambda: vit.vit_bf16_gemm(mln, m["m_fc1_w"], bias=m["m_fc1_b"],
+                                                      epilogue=vit.BEPI_BIAS_GELU, out=mh),
+                            2 * TM * 4608 * 4608, "F16", 4),
+        "merger_fc2_bf16": (lambda: vit.vit_bf16_gemm(mh, m["m_fc2_w"], bias=m["m_fc2_b"], out=mo),
+                            2 * TM * 4096 * 4608, "F16", 4),
+    }
+    res = {}
+    for name, (fn, work, unit, per_step) in cases.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        # back-to-back launches without host gaps: capture `reps` launches in
+        # a graph and time one replay on the stream it replays on
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(reps):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        del graph
+        r = {"us": round(us, 2), "per_step": per_step}
+        if unit == "B":
+            gbs = work / (us * 1e-6) / 1e9
+            r.update(bytes=int(work), gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 3))
+        else:
+            tf = work / (us * 1e-6) / 1e12
+            peak = PEAK_FP8_TFLOPS if unit == "F8" else PEAK_BF16_TFLOPS
+            r.update(flop=int(work), tflops=round(tf, 1), frac_mfma=round(tf / peak, 4))
+        res[name] = r
+        print(f"[bench] {name}: {r}", file=sys.stderr, flush=True)
+    return res
+
+
+if __name__ == "__main__":
+    sys.exit(main())

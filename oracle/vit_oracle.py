@@ -119,7 +119,12 @@ def e4m3_encode(t) -> np.ndarray:
     +-448, zero keeps its sign (-0 -> 0x80)."""
     t = np.asarray(t, dtype=np.float64)
     r = round_to_float_format(np.abs(t), 3, -6, E4M3_MAX, True)
-    mag = np.searchsorted(_E4M3_POS, r).astype(np.uint8)
+    # code of the grid value r: normal r = (1 + f/8) 2^E -> (E + 7) * 8 + f,
+    # subnormal r = f 2^-9 -> f; checked against the decode table below.
+    m, e = np.frexp(r)
+    normal = (e - 1 + 7) * 8 + np.rint((2.0 * m - 1.0) * 8.0)
+    sub = np.rint(r * 512.0)
+    mag = np.where(r >= 2.0 ** -6, normal, sub).astype(np.uint8)
     assert np.all(_E4M3_POS[mag] == r)
     sign = np.signbit(t).astype(np.uint8) << 7
     return (mag | sign).astype(np.uint8)

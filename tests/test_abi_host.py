@@ -1,0 +1,193 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every function include/vit.h declares, and rejects invalid arguments with
+the documented status before anything is enqueued (these calls never reach
+a kernel launch: every case fails validation)."""
+
+import ctypes
+import os
+
+import pytest
+
+import vision_transformer_encoder_amd as vit
+
+OK, NULL, ALIGN, SHAPE, UNSUP, SEQ, WS, ALIAS, HIP = range(9)
+
+A = 0x7f0000000000  # fake, 256-aligned device addresses: never dereferenced
+B = A + (1 << 30)
+C = A + (2 << 30)
+D = A + (3 << 30)
+E = A + (4 << 30)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vit.library_path):
+        pytest.fail("libvit.so is not built (run __graft_entry__.build())")
+    return vit.require_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = vit.declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(vit._SIGS), "binding and header disagree"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.vit_abi_version() == 1
+    for s in range(9):
+        assert lib.vit_status_string(s)
+    assert lib.vit_status_string(0) == b"ok"
+
+
+def _cu(vals):
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    return arr
+
+
+def test_quant_validation(lib):
+    f = lib.vit_quant_fp8_block128
+    assert f(None, 128, 4, 128, 1, B, C, None) == NULL
+    assert f(A + 8, 128, 4, 128, 1, B, C, None) == ALIGN
+    assert f(A, 132, 4, 128, 1, B, C, None) == ALIGN            # ld % 8
+    assert f(A, 128, -1, 128, 1, B, C, None) == SHAPE
+    assert f(A, 64, 4, 128, 1, B, C, None) == SHAPE             # ld < cols
+    assert f(A, 128, 4, 128, 2, B, C, None) == UNSUP
+    assert f(A, 128, 4, 128, 1, A, C, None) == ALIAS
+    assert f(A, 128, 4, 128, 1, B, B + 16, None) == ALIAS       # codes overlap scales
+    assert f(A, 128, 0, 128, 1, None, None, None) == OK          # empty: no-op
+
+
+def test_e4m3_and_layernorm_validation(lib):
+    assert lib.vit_e4m3_encode(A, B, -1, None) == SHAPE
+    assert lib.vit_e4m3_encode(A, B, 0, None) == OK
+    assert lib.vit_e4m3_encode(None, B, 10, None) == NULL
+    assert lib.vit_e4m3_encode(A, A + 16, 100, None) == ALIAS
+    f = lib.vit_layernorm_quant_fp8
+    assert f(A, 1152, B, C, 1e-6, 10, 1000, D, E, None, None) == SHAPE    # D % 128
+    assert f(A, 1152, B, C, -1.0, 10, 1152, D, E, None, None) == SHAPE    # eps < 0
+    assert f(A, 1152, None, C, 1e-6, 10, 1152, D, E, None, None) == NULL
+    assert f(A, 1152, B, C, 1e-6, 10, 1152, D, E, A, None) == ALIAS       # prequant over x
+    assert f(A, 1152, B, C, 1e-6, 0, 1152, D, E, None, None) == OK
+
+
+def test_gemm_validation(lib):
+    f = lib.vit_fp8_block128_gemm
+    assert f(A, B, C, D, 16, 256, 256, None, None, 3, E, None, None, None, None) == UNSUP
+    assert f(A, B, C, D, 16, 0, 256, None, None, 0, E, None, None, None, None) == SHAPE
+    assert f(A, B, C, D, 16, 256, 256, None, None, 1, E, None, None, None, None) == NULL  # residual
+    assert f(A, B, C, D, 16, 256, 256, None, None, 2, None, None, E, None, None) == NULL  # codes
+    assert f(A, B, C, D, 16, 256, 256, None, None, 0, A + 64, None, None, None, None) == ALIAS
+    assert f(A, B, C + 8, D, 16, 256, 256, None, None, 0, E, None, None, None, None) == ALIGN
+    # in-place residual (same pointer) passes validation up to the overlap check of other inputs
+    assert f(A, B, C, D, 16, 256, 256, None, E + 2, 1, E, None, None, None, None) == ALIGN
+    assert f(A, B, C, D, 0, 256, 256, None, None, 0, E, None, None, None, None) == OK
+    g = lib.vit_bf16_gemm
+    assert g(A, 0, B, 16, 64, 12, None, None, 0, C, 64, None) == SHAPE   # K % 8
+    assert g(A, 0, B, 16, 64, 64, None, None, 5, C, 64, None) == UNSUP
+    assert g(A, 0, B, 16, 64, 64, None, None, 0, C, 32, None) == SHAPE   # ld_out < N
+    assert g(A, 0, B, 16, 64, 64, None, None, 0, B, 64, None) == ALIAS
+    assert g(A, 1, None, 16, 64, 64, None, None, 0, C, 64, None) == NULL
+
+
+def test_rope_validation(lib):
+    f = lib.vit_rope2d
+    pos = E
+    assert f(A, A + 2304, 3456, pos, 10, 16, 70, 10000.0, None) == UNSUP
+    assert f(A, A + 2304, 1000, pos, 10, 16, 72, 10000.0, None) == SHAPE     # ld < H*hd
+    assert f(A, A + 2304, 3456, pos, 10, 16, 72, -1.0, None) == SHAPE        # theta
+    assert f(A, A + 16, 3456, pos, 10, 16, 72, 10000.0, None) == ALIAS       # q, k overlap in a row
+    assert f(A, None, 3456, pos, 10, 16, 72, 10000.0, None) == NULL
+    assert f(A, A + 2304, 3456, A + 2304 * 2, 10, 16, 72, 10000.0, None) == ALIAS  # pos inside qkv
+    assert f(A, A + 2304, 3456, pos, 0, 16, 72, 10000.0, None) == OK
+
+
+def test_attention_validation(lib):
+    f = lib.vit_attention
+    cu = _cu([0, 5, 9])
+    bad = _cu([1, 5, 9])
+    dec = _cu([0, 6, 5])
+    args = lambda cuh, ns, T, hd=72, o=D: f(A, A + 2304, A + 4608, 3456, o, 1152, E, cuh, ns, T, 16, hd, 0.1, None)
+    assert args(cu, 2, 9, hd=64) == UNSUP
+    assert args(bad, 2, 9) == SEQ
+    assert args(dec, 2, 5) == SEQ
+    assert args(cu, 2, 10) == SEQ                 # last offset != total
+    assert args(cu, 2, 9, o=A + 64) == ALIAS      # output inside qkv
+    assert f(A, A + 2304, A + 4608, 3456, D, 1152, E, None, 2, 9, 16, 72, 0.1, None) == NULL
+    assert f(A, A + 2304, A + 4608, 3456, D, 1152, E, cu, 2, 9, 16, 72, 0.0, None) == SHAPE
+    assert f(A, A + 2304, A + 4608, 3452, D, 1152, E, cu, 2, 9, 16, 72, 0.1, None) == ALIGN
+    empty = _cu([0])
+    assert f(A, A + 2304, A + 4608, 3456, D, 1152, E, empty, 0, 0, 16, 72, 0.1, None) == OK
+
+
+def test_merge_validation_statuses(lib):
+    f = lib.vit_merge2x2_layernorm
+    grids = _cu([4, 6, 2, 2])
+    odd = _cu([3, 6, 2, 2])
+    assert f(A, 1152, B, odd, 2, 22, C, D, 1e-6, E, None) == SEQ
+    assert f(A, 1152, B, grids, 2, 27, C, D, 1e-6, E, None) == SEQ    # sum h*w != T
+    assert f(A, 4000, B, grids, 2, 28, C, D, 1e-6, E, None) == SHAPE  # 4D > 8192
+    assert f(A, 1152, B, grids, 2, 28, C, D, 1e-6, A + 64, None) == ALIAS
+    assert f(A, 1152, None, grids, 2, 28, C, D, 1e-6, E, None) == NULL
+
+
+def _block_struct(null_field=None, misalign=None):
+    s = vit._BlockW()
+    for i, (name, _) in enumerate(vit._BlockW._fields_):
+        setattr(s, name, A + i * (1 << 24))
+    if null_field:
+        setattr(s, null_field, None)
+    if misalign:
+        setattr(s, misalign, getattr(s, misalign) + 4)
+    return s
+
+
+def test_block_validation(lib):
+    f = lib.vit_block_forward
+    cu = _cu([0, 256])
+    need = lib.vit_block_workspace_size(256)
+    assert need >= 256 * (3456 * 2 + 1152 * 2 + 1152 + 4352)
+    s = _block_struct()
+    X, POS, CU, WSP = B, C, C + 4096, D
+    assert f(ctypes.byref(s), X, 256, POS, CU, cu, 1, WSP, need - 1, None) == WS
+    assert f(ctypes.byref(_block_struct("fc1_codes")), X, 256, POS, CU, cu, 1, WSP, need, None) == NULL
+    assert f(ctypes.byref(_block_struct(misalign="qkv_scales")), X, 256, POS, CU, cu, 1, WSP, need, None) == ALIGN
+    assert f(ctypes.byref(s), X, 256, POS, CU, _cu([0, 255]), 1, WSP, need, None) == SEQ
+    assert f(ctypes.byref(s), X, 256, POS, CU, cu, 1, WSP + 64, need, None) == ALIGN   # 256-B workspace
+    assert f(ctypes.byref(s), X, 256, POS, CU, cu, 1, X, need, None) == ALIAS          # x inside workspace
+    assert f(None, X, 256, POS, CU, cu, 1, WSP, need, None) == NULL
+
+
+def test_encoder_validation(lib):
+    f = lib.vit_encoder_forward
+    w = vit._EncoderW()
+    w.patch_w, w.patch_b = A, A + 4096
+    for b in range(27):
+        w.blocks[b] = _block_struct()
+    for m in range(4):
+        ms = vit._MergerW()
+        for i, (name, _) in enumerate(vit._MergerW._fields_):
+            setattr(ms, name, B + i * (1 << 24))
+        w.mergers[m] = ms
+    grids = _cu([46, 136])
+    T = 6256
+    need = lib.vit_encoder_workspace_size(T, 1)
+    PIX, GD, OUT, WSP = C, C - 4096, D, E
+    assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need - 256, None) == WS
+    assert f(ctypes.byref(w), PIX, None, GD, _cu([46, 135]), 1, 46 * 135, OUT, None, WSP, need, None) == SEQ
+    assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T + 2, OUT, None, WSP, need, None) == SEQ
+    w.mergers[2].fc2_w = None
+    assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need, None) == NULL
+    w.mergers[2].fc2_w = B
+    w.blocks[13].proj_bias = None
+    assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need, None) == NULL
+    w.blocks[13].proj_bias = A
+    assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, WSP + 1024, None, WSP, need, None) == ALIAS
+
+
+def test_workspace_sizes_monotone(lib):
+    sizes = [lib.vit_block_workspace_size(t) for t in (1, 256, 6256, 6684)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    assert lib.vit_block_workspace_size(-1) == 0
+    assert lib.vit_encoder_workspace_size(6256, 1) > lib.vit_block_workspace_size(6256)

@@ -1,0 +1,114 @@
+"""GPU parity of 2D RoPE and of varlen full attention (head_dim 72) against
+the fp64 oracle, with the edge cases of the window packing."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import vision_transformer_encoder_amd as vit
+from gpu_util import announce, assert_close, dev_bf16, host_f64
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, MIN_COS = 2e-2, 0.9995
+
+
+def _qkv_bits(cfg, T, seed=0):
+    return [synth.normal_bf16(cfg, t, seed, (T, 1152)) for t in ("q", "k", "v")]
+
+
+@pytest.mark.parametrize("grids", [[(48, 38)], [(18, 54), (36, 108), (24, 76)]], ids=["48x38", "varlen3"])
+def test_rope2d(gpu, grids):
+    T = sum(h * w for h, w in grids)
+    q, k, _ = _qkv_bits(1, T)
+    qkv = torch.zeros((T, 3456), dtype=torch.bfloat16, device=gpu)
+    qkv[:, :1152] = dev_bf16(q, gpu)
+    qkv[:, 1152:2304] = dev_bf16(k, gpu)
+    pos = synth.positions(grids)
+    announce(f"vit_rope2d T={T}")
+    vit.vit_rope2d(qkv[:, :1152], qkv[:, 1152:2304], torch.from_numpy(pos).to(gpu))
+    res = host_f64(qkv)
+    for name, src, sl in (("q", q, slice(0, 1152)), ("k", k, slice(1152, 2304))):
+        ref = O.rope2d(synth.bf16_bits_to_f64(src), pos)
+        assert_close(res[:, sl], O.bf16(ref), 1e-2, 0.99999, f"rope {name}")
+        # GPU result is within one bf16 rounding of the exact rotation, plus
+        # the fp32 angle error (|p f| 2^-23 scale) times the pair's norm
+        src64 = synth.bf16_bits_to_f64(src).reshape(T, 16, 2, 2, 18)
+        pair = np.sqrt(src64[:, :, :, 0, :] ** 2 + src64[:, :, :, 1, :] ** 2)
+        pair = np.stack([pair, pair], axis=3).reshape(T, 1152)
+        assert np.all(np.abs(res[:, sl] - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-4 * pair)
+    assert np.all(res[:, 2304:] == 0), "v slice must be untouched"
+
+
+def _attention_case(gpu, grids, cfg=1):
+    T = sum(h * w for h, w in grids)
+    q0, k0, v = _qkv_bits(cfg, T)
+    pos = synth.positions(grids)
+    # q, k = bf16(RoPE(q0, k0)) from the oracle: attention isolated from RoPE
+    q = O.bf16(O.rope2d(synth.bf16_bits_to_f64(q0), pos))
+    k = O.bf16(O.rope2d(synth.bf16_bits_to_f64(k0), pos))
+    vf = synth.bf16_bits_to_f64(v)
+    qkv = torch.empty((T, 3456), dtype=torch.bfloat16, device=gpu)
+    qkv[:, :1152] = torch.from_numpy(q).to(gpu).to(torch.bfloat16)
+    qkv[:, 1152:2304] = torch.from_numpy(k).to(gpu).to(torch.bfloat16)
+    qkv[:, 2304:] = dev_bf16(v, gpu)
+    return T, qkv, q, k, vf
+
+
+@pytest.mark.parametrize("grids", [[(48, 38)], [(18, 54), (36, 108), (24, 76)], [(46, 136)]],
+                         ids=["p1824", "varlen_6684", "p6256"])
+def test_attention_parity(gpu, grids):
+    T, qkv, q, k, vf = _attention_case(gpu, grids)
+    cu = synth.cu_seqlens(grids)
+    announce(f"vit_attention T={T} cu={list(cu)}")
+    o = vit.vit_attention(qkv[:, :1152], qkv[:, 1152:2304], qkv[:, 2304:], cu)
+    torch.cuda.synchronize()
+    ref = O.attention(q, k, vf, cu)
+    assert_close(host_f64(o), ref, MAX_REL, MIN_COS, f"attention T={T}")
+
+
+def test_attention_window_edge_cases(gpu):
+    # windows of 1, 63, 64, 65, 127, 128, 129 and 200 tokens plus an empty one
+    lens = [1, 63, 64, 65, 0, 127, 128, 129, 200]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    qb, kb, vb = _qkv_bits(1, T, seed=3)
+    q, k, v = (synth.bf16_bits_to_f64(b) for b in (qb, kb, vb))
+    qkv = torch.cat([dev_bf16(qb, gpu), dev_bf16(kb, gpu), dev_bf16(vb, gpu)], dim=1).contiguous()
+    announce(f"vit_attention edge windows {lens}")
+    o = host_f64(vit.vit_attention(qkv[:, :1152], qkv[:, 1152:2304], qkv[:, 2304:], cu))
+    ref = O.attention(q, k, v, cu)
+    assert_close(o, ref, MAX_REL, MIN_COS, "edge windows")
+    # a one-token window returns its own V exactly (softmax of one score is 1)
+    assert np.array_equal(o[0], v[0])
+
+
+def test_attention_packed_equals_separate_bitwise(gpu):
+    grids = [(18, 54), (24, 76)]
+    T, qkv, _, _, _ = _attention_case(gpu, grids)
+    cu = synth.cu_seqlens(grids)
+    packed = vit.vit_attention(qkv[:, :1152], qkv[:, 1152:2304], qkv[:, 2304:], cu)
+    a = int(cu[1])
+    first = vit.vit_attention(qkv[:a, :1152], qkv[:a, 1152:2304], qkv[:a, 2304:], [0, a])
+    second_qkv = qkv[a:].clone()
+    second = vit.vit_attention(second_qkv[:, :1152], second_qkv[:, 1152:2304], second_qkv[:, 2304:], [0, T - a])
+    assert torch.equal(packed[:a].view(torch.int16), first.view(torch.int16))
+    assert torch.equal(packed[a:].view(torch.int16), second.view(torch.int16))
+
+
+def test_attention_constant_v_and_deterministic(gpu):
+    T = 300
+    qb, kb, _ = _qkv_bits(1, T, seed=9)
+    vrow = synth.normal_bf16(1, "v", 9, (1, 1152))
+    vb = np.repeat(vrow, T, axis=0)
+    qkv = torch.cat([dev_bf16(qb, gpu), dev_bf16(kb, gpu), dev_bf16(vb, gpu)], dim=1).contiguous()
+    o1 = vit.vit_attention(qkv[:, :1152], qkv[:, 1152:2304], qkv[:, 2304:], [0, T])
+    o2 = vit.vit_attention(qkv[:, :1152], qkv[:, 1152:2304], qkv[:, 2304:], [0, T])
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    # softmax weights sum to one: constant V comes back up to rounding
+    vv = synth.bf16_bits_to_f64(vrow)
+    assert np.allclose(host_f64(o1), np.repeat(vv, T, 0), rtol=1e-2, atol=1e-2)

@@ -1,0 +1,95 @@
+"""GPU parity of the FP8 format and quantisers: the E4M3 encoder at every
+rounding decision point, the block-128 quantiser for activations (1 x 128)
+and weights (128 x 128), and LayerNorm fused with the quant.  Codes and
+scales are bit-exact against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import vision_transformer_encoder_amd as vit
+from gpu_util import announce, assert_close, dev_bf16, host_f64, host_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _decision_points() -> np.ndarray:
+    """fp32 values at and around every E4M3 rounding boundary in every binade
+    from 2^-13 to 2^9, plus a strided sweep of all mantissas, both signs,
+    zeros, fp32 subnormals and out-of-range values (saturate)."""
+    vals = []
+    for e in range(-13, 10):
+        base = np.uint32((e + 127) << 23)
+        # boundaries of 3 kept fraction bits lie at multiples of 2^19 in the
+        # fp32 fraction (representable values and midpoints alike)
+        b = (np.arange(0, 1 << 23, 1 << 19, dtype=np.int64)[:, None] + np.arange(-3, 4)[None, :]).ravel()
+        b = b[(b >= 0) & (b < (1 << 23))].astype(np.uint32)
+        vals.append((base | b).view(np.float32))
+        vals.append((base | np.arange(0, 1 << 23, 4099, dtype=np.uint32)).view(np.float32))
+    v = np.concatenate(vals)
+    extra = np.array([0.0, 1e-40, 3e-39, 448.0, 449.0, 464.0, 480.0, 1e6, 3e38], np.float32)
+    v = np.concatenate([v, extra])
+    v = np.concatenate([v, -v])
+    return v.astype(np.float32)
+
+
+def test_e4m3_encoder_decision_points(gpu):
+    x = _decision_points()
+    announce(f"vit_e4m3_encode n={x.size}")
+    codes = host_u8(vit.vit_e4m3_encode(torch.from_numpy(x).to(gpu)))
+    ref = O.e4m3_encode(x.astype(np.float64))
+    bad = np.nonzero(codes != ref)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first x={x[bad[:5]]} gpu={codes[bad[:5]]} ref={ref[bad[:5]]}"
+    # negative zero keeps its sign
+    assert codes[np.nonzero((x == 0) & np.signbit(x))[0][0]] == 0x80
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (7, 200), (300, 1152), (6256, 1152)])
+def test_quant_rows_bit_exact(gpu, rows, cols):
+    bits = synth.normal_bf16(2, "a", rows * 7 + cols, (rows, cols))
+    bits[:, :3] = 0  # some structure: zero columns
+    if rows > 2:
+        bits[2] = 0  # an all-zero row (zero scale)
+    announce(f"vit_quant_fp8_block128 rows={rows} cols={cols}")
+    codes, scales = vit.vit_quant_fp8_block128(dev_bf16(bits, gpu), block_rows=1)
+    rc, rs = O.quantize_block128(synth.bf16_bits_to_f64(bits), 1)
+    assert np.array_equal(host_u8(codes), rc)
+    assert np.array_equal(host_f64(scales), rs)
+
+
+@pytest.mark.parametrize("shape", [(3456, 1152), (1152, 1152), (4304, 1152), (1152, 4304), (130, 200)])
+def test_quant_weight_blocks_bit_exact(gpu, shape):
+    bits = synth.normal_bf16(2, "w", shape[0] + shape[1], shape, std=0.02)
+    announce(f"vit_quant_fp8_block128 weights {shape}")
+    codes, scales = vit.vit_quant_fp8_block128(dev_bf16(bits, gpu), block_rows=128)
+    rc, rs = O.quantize_block128(synth.bf16_bits_to_f64(bits), 128)
+    assert codes.shape == rc.shape and scales.shape == rs.shape
+    assert np.array_equal(host_u8(codes), rc)
+    assert np.array_equal(host_f64(scales), rs)
+
+
+@pytest.mark.parametrize("M", [1, 256, 6256])
+def test_layernorm_quant(gpu, M):
+    x = synth.normal_bf16(0, "x", M, (M, 1152))
+    g = synth.normal_bf16(0, "ln1_g", M, (1152,), std=0.02, mean=1.0)
+    b = synth.normal_bf16(0, "ln1_b", M, (1152,), std=0.01)
+    announce(f"vit_layernorm_quant_fp8 M={M}")
+    codes, scales, pre = vit.vit_layernorm_quant_fp8(dev_bf16(x, gpu), dev_bf16(g, gpu), dev_bf16(b, gpu),
+                                                     1e-6, prequant=True)
+    xf, gf, bf = (synth.bf16_bits_to_f64(t) for t in (x, g, b))
+    ref = O.layernorm(xf, gf, bf)
+    pre_h = host_f64(pre)
+    assert_close(pre_h, ref, 1e-5, 0.99999999, f"LN prequant M={M}")
+    # the oracle's quantiser applied to the GPU's own fp32 pre-quant values
+    rc, rs = O.quantize_block128(pre_h, 1)
+    assert np.array_equal(host_u8(codes), rc)
+    assert np.array_equal(host_f64(scales), rs)
+    # codes taken independently from the fp64 LayerNorm differ by at most
+    # one E4M3 step, and only rarely
+    oc, _ = O.quantize_block128(O.f32(ref), 1)
+    diff = np.abs(O.e4m3_decode(host_u8(codes)) - O.e4m3_decode(oc))
+    flips = int((diff > 0).sum())
+    announce(f"LN-quant code flips vs fp64 pre-quant: {flips} of {codes.numel()}")
+    assert flips <= max(4, codes.numel() // 2000)

@@ -1,0 +1,94 @@
+// Device helpers shared by the gfx950 kernels of libvit: vector types, bf16
+// and OCP E4M3FN conversion, wave reductions, block-128 scale computation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vit {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr float kE4M3Max = 448.0f;
+// Block maxima below 2^-116 give a zero scale: 448 / amax would overflow fp32.
+constexpr float kTinyAmax = 0x1p-116f;
+
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Two bf16 packed in one dword: low half = element 0.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f2bf(float a) { return (uint16_t)(pack_bf16x2(a, 0.0f) & 0xffffu); }
+
+// fp32 -> OCP E4M3FN, nearest-even, saturating at +-448 (v_cvt_pk_fp8_f32 on
+// gfx950 rounds to nearest-even; the clamp makes saturation explicit).
+__device__ __forceinline__ float e4m3_clamp(float x) { return fminf(fmaxf(x, -kE4M3Max), kE4M3Max); }
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), v, true);
+  return (uint32_t)v;
+}
+
+// Block-128 scale: s = amax / 448 and inv = 448 / amax, both correctly
+// rounded fp32 divisions; zero for a (near-)zero block.
+__device__ __forceinline__ void block_scale(float amax, float& s, float& inv) {
+  if (amax < kTinyAmax) {
+    s = 0.0f;
+    inv = 0.0f;
+  } else {
+    s = amax / kE4M3Max;
+    inv = kE4M3Max / amax;
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+// max over aligned groups of 16 lanes
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// tanh-form GELU in fp32.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  float u = k0 * (x + k1 * x * x * x);
+  return 0.5f * x * (1.0f + tanhf(u));
+}
+
+// Load 8 bf16 starting at column c of a row as fp32; columns >= cols read 0.
+// The full-vector path needs the row 16-byte aligned and c % 8 == 0.
+__device__ __forceinline__ void load8_bf16(const uint16_t* __restrict__ row, int c, int cols, float v[8]) {
+  if (c + 8 <= cols) {
+    uint4 w = *reinterpret_cast<const uint4*>(row + c);
+    v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+    v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (c + i < cols) ? bf2f(row[c + i]) : 0.0f;
+  }
+}
+
+}  // namespace vit

@@ -1,0 +1,49 @@
+// Internal launchers of libvit's kernels.  Arguments are validated by the
+// C ABI layer (abi.cpp) before any of these is called; each launcher only
+// enqueues work on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vit {
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t ldx, int rows, int cols, uint8_t* codes,
+                             float* scales, hipStream_t stream);
+hipError_t launch_quant_blocks128(const uint16_t* x, int64_t ldx, int rows, int cols,
+                                  uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
+hipError_t launch_layernorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
+                                  const uint16_t* beta, float eps, int M, int D, uint8_t* codes,
+                                  float* scales, float* prequant, hipStream_t stream);
+
+hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                           const float* w_scales, int M, int N, int K, const uint16_t* bias,
+                           const uint16_t* residual, int epilogue, uint16_t* out,
+                           uint8_t* out_codes, float* out_scales, float* prequant,
+                           hipStream_t stream);
+
+hipError_t launch_bf16_gemm(const void* a, bool a_f32, const uint16_t* w, int M, int N, int K,
+                            const uint16_t* bias, const uint16_t* add, int epilogue,
+                            uint16_t* out, int64_t ld_out, hipStream_t stream);
+
+hipError_t launch_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* pos, int T,
+                         int heads, int head_dim, float theta, hipStream_t stream);
+
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            int64_t ld_qkv, uint16_t* o, int64_t ld_o, const int32_t* cu,
+                            int num_seqs, int total_q_tiles, int heads, float scale,
+                            hipStream_t stream);
+// Number of 128-query tiles the attention launch needs for these windows.
+int attention_q_tiles(const int32_t* cu_host, int num_seqs);
+
+hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_hw,
+                                  int num_images, int T, const uint16_t* gamma,
+                                  const uint16_t* beta, float eps, uint16_t* out,
+                                  hipStream_t stream);
+
+// cu[0..n] and (row, col) per token from the packed image grids.
+hipError_t launch_geometry(const int32_t* grid_hw, int num_images, int T, int32_t* cu,
+                           int32_t* pos, hipStream_t stream);
+
+}  // namespace vit

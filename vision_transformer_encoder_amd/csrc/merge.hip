@@ -1,0 +1,145 @@
+// 2x2 spatial merge fused with the merger LayerNorm, and the per-token
+// geometry of packed images (FlashRT "Qwen3-VL-8B on RTX 5090" page,
+// section 3: "2x2 patch merger -> image_embeds"; spark_model
+// "layers/vision_encoder.rs" page: spatial_merge_size 2, kernel
+// vision_spatial_merge).  The merged row of image j at (R, C) concatenates
+// the tokens (2R, 2C), (2R, 2C+1), (2R+1, 2C), (2R+1, 2C+1) of that image,
+// tokens being in raster order.  HBM-bound: the gather reads each token once.
+#include "common.h"
+#include "kernels.h"
+
+namespace vit {
+
+// One wave per merged row; the 4*D features are NC chunks of 8 per lane.
+template <int NC>
+__global__ __launch_bounds__(256) void merge_layernorm_kernel(const uint16_t* __restrict__ x, int D,
+                                                              const int32_t* __restrict__ grid_hw,
+                                                              int num_images, int TM,
+                                                              const uint16_t* __restrict__ gamma,
+                                                              const uint16_t* __restrict__ beta,
+                                                              float eps, uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int mrow = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (mrow >= TM) return;
+  // locate the image of this merged row
+  int tok0 = 0, mbase = 0, w = 2, local = mrow;
+  for (int j = 0; j < num_images; ++j) {
+    const int h = grid_hw[2 * j], ww = grid_hw[2 * j + 1];
+    const int nm = (h / 2) * (ww / 2);
+    if (mrow < mbase + nm) {
+      w = ww;
+      local = mrow - mbase;
+      break;
+    }
+    mbase += nm;
+    tok0 += h * ww;
+  }
+  const int R = local / (w / 2), C = local % (w / 2);
+  const int src[4] = {tok0 + 2 * R * w + 2 * C, tok0 + 2 * R * w + 2 * C + 1, tok0 + (2 * R + 1) * w + 2 * C,
+                      tok0 + (2 * R + 1) * w + 2 * C + 1};
+  const int D4 = 4 * D;
+  const int nchunk = D4 >> 3, cpd = D >> 3;
+  float v[NC][8];
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int ch = i * 64 + lane;
+    if (ch < nchunk) {
+      const int slot = ch / cpd, cc = ch % cpd;
+      load8_bf16(x + (int64_t)src[slot] * D, cc * 8, D, v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += v[i][j];
+  }
+  const float mean = wave_sum(sum) / (float)D4;
+  float sq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    if (i * 64 + lane < nchunk) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float d = v[i][j] - mean;
+        sq += d * d;
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D4 + eps);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int ch = i * 64 + lane;
+    if (ch < nchunk) {
+      float gg[8], bb[8];
+      load8_bf16(gamma, ch * 8, D4, gg);
+      load8_bf16(beta, ch * 8, D4, bb);
+      uint4 o;
+      o.x = pack_bf16x2((v[i][0] - mean) * rstd * gg[0] + bb[0], (v[i][1] - mean) * rstd * gg[1] + bb[1]);
+      o.y = pack_bf16x2((v[i][2] - mean) * rstd * gg[2] + bb[2], (v[i][3] - mean) * rstd * gg[3] + bb[3]);
+      o.z = pack_bf16x2((v[i][4] - mean) * rstd * gg[4] + bb[4], (v[i][5] - mean) * rstd * gg[5] + bb[5]);
+      o.w = pack_bf16x2((v[i][6] - mean) * rstd * gg[6] + bb[6], (v[i][7] - mean) * rstd * gg[7] + bb[7]);
+      *reinterpret_cast<uint4*>(out + (int64_t)mrow * D4 + ch * 8) = o;
+    }
+  }
+}
+
+hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_hw,
+                                  int num_images, int T, const uint16_t* gamma,
+                                  const uint16_t* beta, float eps, uint16_t* out,
+                                  hipStream_t stream) {
+  const int TM = T / 4;
+  if (TM == 0) return hipSuccess;
+  const int nc = (4 * D / 8 + 63) / 64;
+  const dim3 grid((TM + 3) / 4);
+#define VIT_ML(N)                                                                                      \
+  case N:                                                                                             \
+    merge_layernorm_kernel<N><<<grid, 256, 0, stream>>>(x, D, grid_hw, num_images, TM, gamma, beta, \
+                                                        eps, out);                                 \
+    break;
+  switch (nc) {
+    VIT_ML(1) VIT_ML(2) VIT_ML(3) VIT_ML(4) VIT_ML(5) VIT_ML(6) VIT_ML(7) VIT_ML(8)
+    VIT_ML(9) VIT_ML(10) VIT_ML(11) VIT_ML(12) VIT_ML(13) VIT_ML(14) VIT_ML(15) VIT_ML(16)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef VIT_ML
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- geometry
+__global__ void cu_from_grids_kernel(const int32_t* __restrict__ grid_hw, int n, int32_t* __restrict__ cu) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    int acc = 0;
+    cu[0] = 0;
+    for (int j = 0; j < n; ++j) {
+      acc += grid_hw[2 * j] * grid_hw[2 * j + 1];
+      cu[j + 1] = acc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void positions_kernel(const int32_t* __restrict__ grid_hw,
+                                                        const int32_t* __restrict__ cu, int n, int T,
+                                                        int32_t* __restrict__ pos) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int lo = 0, hi = n - 1;  // last image j with cu[j] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int w = grid_hw[2 * lo + 1];
+  const int local = t - cu[lo];
+  pos[2 * t] = local / w;
+  pos[2 * t + 1] = local % w;
+}
+
+hipError_t launch_geometry(const int32_t* grid_hw, int num_images, int T, int32_t* cu,
+                           int32_t* pos, hipStream_t stream) {
+  cu_from_grids_kernel<<<1, 64, 0, stream>>>(grid_hw, num_images, cu);
+  if (T > 0) positions_kernel<<<(T + 255) / 256, 256, 0, stream>>>(grid_hw, cu, num_images, T, pos);
+  return hipGetLastError();
+}
+
+}  // namespace vit
