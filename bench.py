@@ -125,6 +125,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel event timings")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--kernel", default=None,
+                    help="only launch this kernel of the step (eagerly, --kernel-reps times) and report its "
+                         "timing: the driver of the per-kernel counter profiles")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -145,6 +148,15 @@ def main() -> int:
     nimg = len(grids)
 
     print(f"[bench] workload {args.workload}: T={T}, images={nimg}", file=sys.stderr, flush=True)
+    if args.kernel:
+        # weights of one block and one merger suffice for a single kernel
+        ep = synth.EncoderParams(patch=synth.patch_params(cfg), blocks=[synth.block_params(cfg, 0)] * 27,
+                                 mergers=[synth.merger_params(cfg, 0)] * 4)
+        W = vit.EncoderWeights(ep.patch, ep.blocks, ep.mergers, dev)
+        k = time_kernels(vit, W, T, grids, dev, args.kernel_reps, [h * w for h, w in grids],
+                         only=args.kernel, eager=True)
+        print(json.dumps({"kernel": args.kernel, "workload": args.workload, **k[args.kernel]}), flush=True)
+        return 0
     ep = synth.encoder_params(cfg)
     W = vit.EncoderWeights(ep.patch, ep.blocks, ep.mergers, dev)
     px = torch.from_numpy(synth.pixels(cfg, T)).to(dev)
@@ -221,7 +233,19 @@ def main() -> int:
     return 0 if ok else 1
 
 
-def time_kernels(vit, W, T, grids, dev, reps, seq):
+def _kernel_record(us, per_step, work, unit):
+    r = {"us": round(us, 2), "per_step": per_step}
+    if unit == "B":
+        gbs = work / (us * 1e-6) / 1e9
+        r.update(bytes=int(work), gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 3))
+    else:
+        tf = work / (us * 1e-6) / 1e12
+        peak = PEAK_FP8_TFLOPS if unit == "F8" else PEAK_BF16_TFLOPS
+        r.update(flop=int(work), tflops=round(tf, 1), frac_mfma=round(tf / peak, 4))
+    return r
+
+
+def time_kernels(vit, W, T, grids, dev, reps, seq, only=None, eager=False):
     """Average launch duration of each kernel of the step, at the shapes and
     launch configuration the tower uses, measured with HIP events on the
     current stream (the stream every launch goes to)."""
@@ -251,6 +275,8 @@ def time_kernels(vit, W, T, grids, dev, reps, seq):
     mo = torch.empty((TM, 4096), dtype=torch.bfloat16, device=dev)
     px = torch.rand((T, 1536), device=dev) * 2 - 1
     xp = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    cpy_src = torch.randn((T, 4096), device=dev).to(torch.bfloat16)
+    cpy_dst = torch.empty_like(cpy_src)
     att_flop = sum(4 * p * p * H for p in seq)
     gemm = lambda n, k: 2 * T * n * k
     B = 27
@@ -286,11 +312,28 @@ def time_kernels(vit, W, T, grids, dev, reps, seq):
         "merger_fc2_bf16": (lambda: vit.vit_bf16_gemm(mh, m["m_fc2_w"], bias=m["m_fc2_b"], out=mo),
                             2 * TM * 4096 * 4608, "F16", 4),
     }
+    # a plain copy of known size: the reference for the HBM byte counters
+    cases["copy_calibration"] = (lambda: cpy_dst.copy_(cpy_src), 2 * cpy_src.numel() * 2, "B", 0)
     res = {}
     for name, (fn, work, unit, per_step) in cases.items():
+        if only is None and per_step == 0:
+            continue
+        if only is not None and name != only:
+            continue
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
+        if eager:
+            stream = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            res[name] = _kernel_record(us, per_step, work, unit)
+            continue
         # back-to-back launches without host gaps: capture `reps` launches in
         # a graph and time one replay on the stream it replays on
         graph = torch.cuda.CUDAGraph()
@@ -307,14 +350,7 @@ def time_kernels(vit, W, T, grids, dev, reps, seq):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         del graph
-        r = {"us": round(us, 2), "per_step": per_step}
-        if unit == "B":
-            gbs = work / (us * 1e-6) / 1e9
-            r.update(bytes=int(work), gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 3))
-        else:
-            tf = work / (us * 1e-6) / 1e12
-            peak = PEAK_FP8_TFLOPS if unit == "F8" else PEAK_BF16_TFLOPS
-            r.update(flop=int(work), tflops=round(tf, 1), frac_mfma=round(tf / peak, 4))
+        r = _kernel_record(us, per_step, work, unit)
         res[name] = r
         print(f"[bench] {name}: {r}", file=sys.stderr, flush=True)
     return res

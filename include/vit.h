@@ -136,8 +136,8 @@ int vit_layernorm_quant_fp8(const uint16_t* x, int64_t ld_x, const uint16_t* gam
  *                          [M, Np/128] = block quant of y per row, per 128
  *                          columns; prequant_debug NULL or [M, Np] fp32 y.
  * bias: [N] bf16 or NULL (zero).  Unused output pointers may be NULL.
- * All leading dimensions are the logical widths (packed rows).
- * M == 0 is a no-op.
+ * All leading dimensions are the logical widths (packed rows).  M * Kp and
+ * Np * Kp must each be below 2^32 (VIT_ERR_SHAPE).  M == 0 is a no-op.
  * ------------------------------------------------------------------- */
 #define VIT_EPI_BIAS 0
 #define VIT_EPI_BIAS_RESIDUAL 1
@@ -159,7 +159,7 @@ int vit_fp8_block128_gemm(const uint8_t* a, const float* a_scales,
  * as it is loaded: the fp32 pixel buffer of the patch embedding).
  * w: [N, K] bf16; bias: [N] bf16 or NULL; add: [M, N] bf16 (BIAS_ADD only,
  * NULL = no add); out: [M, ld_out] bf16, ld_out >= N.
- * K % 8 == 0.  M == 0 is a no-op.
+ * K % 8 == 0; M * K and N * K below 2^32.  M == 0 is a no-op.
  * ------------------------------------------------------------------- */
 #define VIT_BEPI_BIAS 0
 #define VIT_BEPI_BIAS_GELU 1
@@ -194,7 +194,8 @@ int vit_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* pos_rc, int 
  * cu_seqlens_dev / cu_seqlens_host: the same num_seqs+1 int32 offsets on the
  * device and on the host (the host copy is read for validation and launch
  * sizing only); cu[0] = 0, non-decreasing, cu[num_seqs] = total_tokens.
- * head_dim must be 72 (VIT_ERR_UNSUPPORTED otherwise); ld_qkv, ld_o % 8 == 0.
+ * head_dim must be 72 (VIT_ERR_UNSUPPORTED otherwise); ld_qkv, ld_o % 8 == 0;
+ * total_tokens * ld_qkv < 2^31.
  * ------------------------------------------------------------------- */
 int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
                   uint16_t* o, int64_t ld_o,

@@ -268,6 +268,7 @@ int vit_fp8_block128_gemm(const uint8_t* a, const float* a_scales, const uint8_t
   for (const void* p : all)
     if (p && !al16(p)) return VIT_ERR_ALIGN;
   const int Kp = ceil128(K), Np = ceil128(N);
+  if ((uint64_t)M * Kp >= ((uint64_t)1 << 32) || (uint64_t)Np * Kp >= ((uint64_t)1 << 32)) return VIT_ERR_SHAPE;
   const size_t ab = (size_t)M * Kp, asb = (size_t)M * (Kp / 128) * 4, wb = (size_t)Np * Kp,
                wsb = (size_t)(Np / 128) * (Kp / 128) * 4, bb = bias ? (size_t)N * 2 : 0;
   const size_t rb = (size_t)M * N * 2;
@@ -298,6 +299,7 @@ int vit_bf16_gemm(const void* a, int a_is_f32, const uint16_t* w, int M, int N, 
   if (M < 0 || N < 1 || K < 8 || (K % 8) || M > kMaxTokens * 4 || N > kMaxDim || K > kMaxDim || ld_out < N)
     return VIT_ERR_SHAPE;
   if (epilogue < VIT_BEPI_BIAS || epilogue > VIT_BEPI_BIAS_ADD) return VIT_ERR_UNSUPPORTED;
+  if ((uint64_t)M * K >= ((uint64_t)1 << 32) || (uint64_t)N * K >= ((uint64_t)1 << 32)) return VIT_ERR_SHAPE;
   if (M == 0) return VIT_OK;
   if (!a || !w || !out) return VIT_ERR_NULL;
   const void* all[] = {a, w, bias, add, out};
@@ -352,6 +354,7 @@ int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64
   if (!q || !k || !v || !o || !cu_seqlens_dev) return VIT_ERR_NULL;
   if (!al16(q) || !al16(k) || !al16(v) || !al16(o) || !al16(cu_seqlens_dev) || (ld_qkv & 7) || (ld_o & 7))
     return VIT_ERR_ALIGN;
+  if ((int64_t)total_tokens * ld_qkv >= ((int64_t)1 << 31)) return VIT_ERR_SHAPE;
   const size_t ib = ((size_t)(total_tokens - 1) * ld_qkv + width) * 2;
   const size_t ob = ((size_t)(total_tokens - 1) * ld_o + width) * 2;
   if (overlap(o, ob, q, ib) || overlap(o, ob, k, ib) || overlap(o, ob, v, ib)) return VIT_ERR_ALIAS;

@@ -10,16 +10,25 @@
 //  * Everything is computed transposed, S^T = K Q^T and O^T = V^T P^T, with
 //    v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane holds
 //    one column (lane % 32) and 16 rows, so every lane owns ONE query: the
-//    row max / row sum of the softmax and the rescale of O stay in the
-//    lane's registers, plus one cross-half exchange (lane ^ 32) per tile.
+//    row max and the rescale of O stay in the lane's registers, plus one
+//    cross-half exchange (lane ^ 32) per tile.
 //  * P never leaves registers: the 16 key-rows a lane holds in S^T are, in
 //    order, the 8+8 k-slots of the B operand of two PV MFMAs (the key order
 //    inside an MFMA is a free permutation as long as V^T uses the same one).
 //  * head_dim 72 is padded to 80 for Q K^T (5 MFMAs of K=16) and to 96 rows
-//    for V^T (3 row tiles of 32); the pad lanes read zeros kept in LDS.
-//  * K tiles (64 keys x 80) and V^T tiles (96 x 64) are double-buffered in
-//    LDS; the next tile's global loads are issued before the current
-//    tile's MFMAs.  Row strides (88 and 68 bf16) make the ds_read_b128 /
+//    for V^T (3 row tiles of 32).  Of the third V^T tile, row 72 is all ones:
+//    its output row is the softmax denominator (sum of the bf16 P actually
+//    multiplied), accumulated and rescaled by the MFMA for free; rows 73..95
+//    are zero.  These rows come from registers, not LDS.
+//  * Software pipeline across key tiles: while the VALU turns S(j) into P(j)
+//    (exp2 with the scale folded in), the MFMA unit already computes S(j+1);
+//    then the PV MFMAs of tile j run.  K and V^T tiles live in a 3-buffer LDS
+//    ring (tile j: V^T read, tile j+1: K read, tile j+2: being written), one
+//    barrier per tile; global loads of tile j+2 are in flight during tile j.
+//  * The running max is only raised (and O rescaled) when a row max grows
+//    by more than 2^8 over it: exact after the final division by the row
+//    sum, and it removes the per-tile rescale of 48 accumulators.
+//  * Row strides in LDS (88 bf16 for K, 68 for V^T) keep the ds_read_b128 /
 //    ds_read_b64 operand fetches bank-conflict free.
 //  * Workgroup id -> (q tile, head) with head fastest: ids that share a head
 //    are congruent mod 8, so each XCD (ids round-robin over 8 XCDs) serves
@@ -35,85 +44,143 @@ constexpr int kBQ = 128;          // queries per workgroup
 constexpr int kBK = 64;           // keys per tile
 constexpr int kKS = 88;           // K row stride in LDS (bf16): 80 used
 constexpr int kVS = 68;           // V^T row stride in LDS (bf16): 64 used
-constexpr int kVRows = 96;        // V^T rows (head_dim padded to 3 x 32)
 constexpr int kKBuf = kBK * kKS;  // elements per K buffer
-constexpr int kVBuf = kVRows * kVS;
+constexpr int kVBuf = kHD * kVS;  // V^T rows 0..71 only
+constexpr int kStages = 3;
+constexpr float kLazy = 8.0f;     // rescale only when the max grows by > 2^8
 }  // namespace
 
 __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
 
-// Loads of one K/V tile into registers.  K: 64 rows x 9 chunks of 16 B = 576
-// chunks, up to 3 per thread.  V: 16 groups of 4 keys x 9 chunks of 8 d =
-// 144 items (threads 0..143), 4 x 16 B each.  Keys past the window end are
-// clamped to its last key (finite data; their scores are masked).
+// Staging of one K/V tile.  K: 64 rows x 9 chunks of 16 B = 576 chunks,
+// thread t owns chunks t, t+256 and (t < 64) t+512.  V: 16 groups of 4 keys
+// x 9 chunks of 8 d = 144 items (threads 0..143), 4 x 16 B each, transposed
+// into V^T on the way to LDS.  All offsets are fixed per thread; only the
+// last tile of a window clamps its keys to the window (finite data; their
+// scores are masked).
 struct KVRegs {
-  uint4 k[3];
-  uint4 v[4];
+  u32x4_t k0, k1, k2;
+  u32x4_t v[4];
 };
 
-__device__ __forceinline__ void load_kv(KVRegs& r, const uint16_t* __restrict__ kbase,
-                                        const uint16_t* __restrict__ vbase, int64_t ld, int key0,
-                                        int nkeys, int tid) {
+struct KVPlan {
+  int krow[3];      // K tile rows of the three chunks
+  int32_t kgoff[3]; // their global element offsets within a tile (row * ld + col * 8)
+  int klds[3];      // their LDS element offsets
+  int vkg, vgoff;   // V: key group and global offset of key 4*vkg, chunk vc
+  int vlds;         // V^T LDS offset of row 8*vc, column 4*vkg
+};
+
+__device__ __forceinline__ KVPlan make_plan(int tid, int64_t ld) {
+  KVPlan p;
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
-    const int c = tid + 256 * i;
-    if (c < 576) {
-      const int row = c / 9, col = c % 9;
-      const int key = min(key0 + row, nkeys - 1);
-      r.k[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)key * ld + col * 8);
-    }
+    const int c = min(tid + 256 * i, 575);
+    const int row = c / 9, col = c % 9;
+    p.krow[i] = row;
+    p.kgoff[i] = (int32_t)(row * ld + col * 8);
+    p.klds[i] = row * kKS + col * 8;
   }
-  if (tid < 144) {
-    const int c = tid % 9, kg = tid / 9;
+  const int vc = tid % 9;
+  p.vkg = tid / 9;
+  p.vgoff = (int32_t)(4 * p.vkg * ld + vc * 8);
+  p.vlds = 8 * vc * kVS + 4 * p.vkg;
+  return p;
+}
+
+__device__ __forceinline__ void load_kv(KVRegs& r, const KVPlan& p, const uint16_t* __restrict__ kbase,
+                                        const uint16_t* __restrict__ vbase, int64_t ld, int key0, int nkeys,
+                                        int tid) {
+  const uint16_t* kt = kbase + (int64_t)key0 * ld;
+  const uint16_t* vt = vbase + (int64_t)key0 * ld;
+  if (key0 + kBK <= nkeys) {
+    r.k0 = *reinterpret_cast<const u32x4_t*>(kt + p.kgoff[0]);
+    r.k1 = *reinterpret_cast<const u32x4_t*>(kt + p.kgoff[1]);
+    if (tid < 64) r.k2 = *reinterpret_cast<const u32x4_t*>(kt + p.kgoff[2]);
+    if (tid < 144) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(key0 + 4 * kg + i, nkeys - 1);
-      r.v[i] = *reinterpret_cast<const uint4*>(vbase + (int64_t)key * ld + c * 8);
+      for (int i = 0; i < 4; ++i) r.v[i] = *reinterpret_cast<const u32x4_t*>(vt + p.vgoff + i * ld);
+    }
+  } else {
+    // last, partial tile: keys past the window end read its last key
+    const int last = nkeys - 1 - key0;
+    auto kclamp = [&](int i) {
+      const int d = min(p.krow[i], last) - p.krow[i];
+      return *reinterpret_cast<const u32x4_t*>(kt + p.kgoff[i] + (int64_t)d * ld);
+    };
+    r.k0 = kclamp(0);
+    r.k1 = kclamp(1);
+    if (tid < 64) r.k2 = kclamp(2);
+    if (tid < 144) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 4 * p.vkg + i;
+        const int d = min(key, last) - key;
+        r.v[i] = *reinterpret_cast<const u32x4_t*>(vt + p.vgoff + (int64_t)(i + d) * ld);
+      }
     }
   }
 }
 
-__device__ __forceinline__ void store_kv(const KVRegs& r, uint16_t* __restrict__ ks,
+__device__ __forceinline__ void store_kv(const KVRegs& r, const KVPlan& p, uint16_t* __restrict__ ks,
                                          uint16_t* __restrict__ vt, int tid) {
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int c = tid + 256 * i;
-    if (c < 576) {
-      const int row = c / 9, col = c % 9;
-      *reinterpret_cast<uint4*>(ks + row * kKS + col * 8) = r.k[i];
-    }
-  }
+  *reinterpret_cast<u32x4_t*>(ks + p.klds[0]) = r.k0;
+  *reinterpret_cast<u32x4_t*>(ks + p.klds[1]) = r.k1;
+  if (tid < 64) *reinterpret_cast<u32x4_t*>(ks + p.klds[2]) = r.k2;
   if (tid < 144) {
-    const int c = tid % 9, kg = tid / 9;
-    // r.v[i] holds d = 8c..8c+7 of key 4kg+i; write V^T[8c+j][4kg .. 4kg+3].
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.v[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.v[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.v[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.v[3]);
+    // r.v[i] holds d = 8vc..8vc+7 of key 4vkg+i (dword j = d 8vc+2j, 8vc+2j+1);
+    // write V^T[8vc+2j (+1)][4vkg .. 4vkg+3].
+    const uint32_t w[4][4] = {{r.v[0][0], r.v[0][1], r.v[0][2], r.v[0][3]},
+                              {r.v[1][0], r.v[1][1], r.v[1][2], r.v[1][3]},
+                              {r.v[2][0], r.v[2][1], r.v[2][2], r.v[2][3]},
+                              {r.v[3][0], r.v[3][1], r.v[3][2], r.v[3][3]}};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // d = 8c + 2j (low halves) and 8c + 2j + 1 (high halves)
       uint2 lo, hi;
-      lo.x = (w0[j] & 0xffffu) | (w1[j] << 16);
-      lo.y = (w2[j] & 0xffffu) | (w3[j] << 16);
-      hi.x = (w0[j] >> 16) | (w1[j] & 0xffff0000u);
-      hi.y = (w2[j] >> 16) | (w3[j] & 0xffff0000u);
-      *reinterpret_cast<uint2*>(vt + (8 * c + 2 * j) * kVS + 4 * kg) = lo;
-      *reinterpret_cast<uint2*>(vt + (8 * c + 2 * j + 1) * kVS + 4 * kg) = hi;
+      lo.x = (w[0][j] & 0xffffu) | (w[1][j] << 16);
+      lo.y = (w[2][j] & 0xffffu) | (w[3][j] << 16);
+      hi.x = (w[0][j] >> 16) | (w[1][j] & 0xffff0000u);
+      hi.y = (w[2][j] >> 16) | (w[3][j] & 0xffff0000u);
+      *reinterpret_cast<uint2*>(vt + p.vlds + 2 * j * kVS) = lo;
+      *reinterpret_cast<uint2*>(vt + p.vlds + (2 * j + 1) * kVS) = hi;
     }
   }
 }
 
-__global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restrict__ q,
-                                                        const uint16_t* __restrict__ k,
-                                                        const uint16_t* __restrict__ v, int64_t ld,
-                                                        uint16_t* __restrict__ o, int64_t ldo,
-                                                        const int32_t* __restrict__ cu, int num_seqs,
-                                                        int heads, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks_mem[2 * kKBuf];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_mem[2 * kVBuf];
+// S^T tile (64 keys x 32 queries) = K Q^T from the K buffer.
+__device__ __forceinline__ void qk_tile(f32x16_t s[2], const uint16_t* __restrict__ ks, const bf16x8_t qf[5],
+                                        int l32, int g) {
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt) {
+    s[jt] = f32x16_t{};
+    const uint16_t* kr = ks + (32 * jt + l32) * kKS + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < 5; ++kc)
+      s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(kr + 16 * kc), qf[kc], s[jt], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void mask_tile(f32x16_t s[2], int key0, int nkeys, int g) {
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int key = key0 + 32 * jt + 8 * (rr >> 2) + 4 * g + (rr & 3);
+      if (key >= nkeys) s[jt][rr] = -INFINITY;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v, int64_t ld,
+                                                           uint16_t* __restrict__ o, int64_t ldo,
+                                                           const int32_t* __restrict__ cu, int num_seqs,
+                                                           int heads, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks_mem[kStages * kKBuf];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_mem[kStages * kVBuf];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -139,15 +206,9 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   const uint16_t* kbase = k + (int64_t)seq_begin * ld + hoff;
   const uint16_t* vbase = v + (int64_t)seq_begin * ld + hoff;
 
-  // ---- zero the padding of both LDS buffers (K cols 72..79, V^T rows 72..95)
-  for (int i = tid; i < 2 * kBK; i += 256) {
+  // ---- zero the K padding columns 72..79 of every stage (never overwritten)
+  for (int i = tid; i < kStages * kBK; i += 256)
     *reinterpret_cast<uint4*>(ks_mem + (i / kBK) * kKBuf + (i % kBK) * kKS + 72) = make_uint4(0, 0, 0, 0);
-  }
-  for (int i = tid; i < 2 * 24 * (kVS / 4); i += 256) {
-    const int b = i / (24 * (kVS / 4)), rem = i % (24 * (kVS / 4));
-    *reinterpret_cast<uint2*>(vt_mem + b * kVBuf + (72 + rem / (kVS / 4)) * kVS + 4 * (rem % (kVS / 4))) =
-        make_uint2(0, 0);
-  }
 
   // ---- Q^T operand: lane holds query q_row, d = 16kc + 8g .. +8 (zero past 72)
   const int q_local = tile * kBQ + wave * 32 + l32;
@@ -158,66 +219,61 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 #pragma unroll
     for (int kc = 0; kc < 5; ++kc) {
       const int d = 16 * kc + 8 * g;
-      if (d < kHD) {
-        qf[kc] = ld_bf16x8(qp + d);
-      } else {
-        qf[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-      }
+      qf[kc] = d < kHD ? ld_bf16x8(qp + d) : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
     }
   }
+
+  // third V^T row tile: rows 64..71 from LDS (lanes l32 < 8), row 72 = ones
+  // (softmax denominator), rows 73..95 = zero.  Lanes >= 8 read the row of
+  // lane l32 % 8 (a broadcast) and replace it.
+  const int vrow2 = 64 + (l32 & 7);
+  const uint32_t tail_fill = (l32 == 8) ? 0x3f803f80u : 0u;
+  const bool tail_real = l32 < 8;
 
   f32x16_t acc[3];
 #pragma unroll
   for (int dt = 0; dt < 3; ++dt) acc[dt] = f32x16_t{};
   float m_run = -INFINITY;  // running max of scaled scores (log2 units)
-  float l_run = 0.0f;       // lane-partial running sum
 
   const int ntiles = (seq_len + kBK - 1) / kBK;
+  const KVPlan plan = make_plan(tid, ld);
   KVRegs r;
-  load_kv(r, kbase, vbase, ld, 0, seq_len, tid);
-  store_kv(r, ks_mem, vt_mem, tid);
+  load_kv(r, plan, kbase, vbase, ld, 0, seq_len, tid);
+  store_kv(r, plan, ks_mem, vt_mem, tid);
+  if (ntiles > 1) {
+    load_kv(r, plan, kbase, vbase, ld, kBK, seq_len, tid);
+    store_kv(r, plan, ks_mem + kKBuf, vt_mem + kVBuf, tid);
+  }
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const uint16_t* ks = ks_mem + buf * kKBuf;
-    const uint16_t* vt = vt_mem + buf * kVBuf;
-    if (it + 1 < ntiles) load_kv(r, kbase, vbase, ld, (it + 1) * kBK, seq_len, tid);
+  f32x16_t s_cur[2], s_nxt[2];
+  qk_tile(s_cur, ks_mem, qf, l32, g);
+  if (seq_len < kBK) mask_tile(s_cur, 0, seq_len, g);
 
-    // ---- S^T = K Q^T for 2 x 32 keys
-    f32x16_t s[2];
+  int bv = 0;  // stage holding tile it
+  for (int it = 0; it < ntiles; ++it) {
+    const int bk = bv == kStages - 1 ? 0 : bv + 1;  // stage of tile it+1
+    const int bw = bk == kStages - 1 ? 0 : bk + 1;  // stage for tile it+2
+    const bool more2 = it + 2 < ntiles;
+    if (more2) load_kv(r, plan, kbase, vbase, ld, (it + 2) * kBK, seq_len, tid);
+
+    // ---- row max of S(it); lazy rescale of O
+    float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      s[jt] = f32x16_t{};
-      const uint16_t* kr = ks + (32 * jt + l32) * kKS + 8 * g;
+    for (int rr = 2; rr < 16; ++rr) mx = fmaxf(mx, s_cur[0][rr]);
 #pragma unroll
-      for (int kc = 0; kc < 5; ++kc) {
-        s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(kr + 16 * kc), qf[kc], s[jt], 0, 0, 0);
-      }
+    for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s_cur[1][rr]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 3; ++dt) acc[dt] *= alpha;
     }
-    // ---- mask keys past the window end (last tile only)
-    const int key0 = it * kBK;
-    if (key0 + kBK > seq_len) {
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int key = key0 + 32 * jt + 8 * (rr >> 2) + 4 * g + (rr & 3);
-          if (key >= seq_len) s[jt][rr] = -INFINITY;
-        }
-      }
-    }
-    // ---- online softmax, one query per lane
-    float mx = s[0][0];
-#pragma unroll
-    for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s[0][rr]);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[1][rr]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.0f;
+
+    // ---- P(it) = exp2(S * scale - m) on the VALU, S(it+1) on the MFMA unit
+    qk_tile(s_nxt, ks_mem + bk * kKBuf, qf, l32, g);
     bf16x8_t pb[2][2];
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
@@ -225,10 +281,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
       for (int h = 0; h < 2; ++h) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[jt][8 * h + j], scale_log2, -m_new));
-          psum += p[j];
-        }
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[jt][8 * h + j], scale_log2, -m_run));
         uint4 w;
         w.x = pack_bf16x2(p[0], p[1]);
         w.y = pack_bf16x2(p[2], p[3]);
@@ -237,35 +290,39 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
         pb[jt][h] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < 3; ++dt) acc[dt] *= alpha;
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T (tile it)
+    const uint16_t* vt = vt_mem + bv * kVBuf;
 #pragma unroll
     for (int dt = 0; dt < 3; ++dt) {
-      const uint16_t* vr = vt + (32 * dt + l32) * kVS + 4 * g;
+      const uint16_t* vr = vt + (dt < 2 ? 32 * dt + l32 : vrow2) * kVS + 4 * g;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int kb = 32 * jt + 16 * h;
-          uint4 w;
           const uint2 a0 = *reinterpret_cast<const uint2*>(vr + kb);
           const uint2 a1 = *reinterpret_cast<const uint2*>(vr + kb + 8);
-          w.x = a0.x; w.y = a0.y; w.z = a1.x; w.w = a1.y;
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb[jt][h],
-                                                           acc[dt], 0, 0, 0);
+          uint4 w = make_uint4(a0.x, a0.y, a1.x, a1.y);
+          if (dt == 2 && !tail_real) w = make_uint4(tail_fill, tail_fill, tail_fill, tail_fill);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb[jt][h], acc[dt],
+                                                           0, 0, 0);
         }
       }
     }
 
-    if (it + 1 < ntiles) store_kv(r, ks_mem + (buf ^ 1) * kKBuf, vt_mem + (buf ^ 1) * kVBuf, tid);
+    if ((it + 2) * kBK > seq_len && it + 1 < ntiles) mask_tile(s_nxt, (it + 1) * kBK, seq_len, g);
+    if (more2) store_kv(r, plan, ks_mem + bw * kKBuf, vt_mem + bw * kVBuf, tid);
     __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) s_cur[jt] = s_nxt[jt];
+    bv = bk;
   }
 
-  // ---- normalise and store: lane holds query q_local, d = 32dt + 8(rr/4) + 4g + rr%4
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---- normalise and store: lane holds query q_local, d = 32dt + 8(rr/4) + 4g + rr%4;
+  // the row sum sits in acc[2][4] of the g == 0 half (row 72 of O^T).
+  const float l_lo = acc[2][4];
+  const float l_tot = __shfl(l_lo, l32);
   const float inv_l = 1.0f / l_tot;
   if (q_local < seq_len) {
     uint16_t* op = o + (int64_t)(seq_begin + q_local) * ldo + hoff;

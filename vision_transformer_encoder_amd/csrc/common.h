@@ -13,6 +13,9 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+// Plain vector (not HIP's uint4 struct) so register arrays of it stay in
+// registers instead of being demoted to scratch.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kE4M3Max = 448.0f;
 // Block maxima below 2^-116 give a zero scale: 448 / amax would overflow fp32.

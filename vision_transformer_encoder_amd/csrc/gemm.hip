@@ -9,17 +9,25 @@
 //
 // gfx950 design: 256 threads = 4 waves on a 128 (n) x 128 (m) output tile,
 // 2 x 2 waves of 64 x 64, v_mfma_f32_32x32x64_f8f6f4 (FP8) or
-// v_mfma_f32_32x32x16_bf16.  The WEIGHT is the MFMA A operand and the
-// ACTIVATION the B operand, so in the 32x32 accumulator layout a lane holds
-// one token row (lane % 32) and 4 runs of 4 consecutive output features:
-// epilogue stores are 8-byte runs, the per-row FP8 requant amax is mostly
-// in-lane, and the per-row activation scale is one register per m-tile.
-// FP8 block scaling: each 128-deep K block is one MFMA chain started from
-// zero (the MFMA's internal sum is not fp32-exact, so partial sums are
-// promoted every 128 K), then acc += partial * sA[m, kb] * sW[n/128, kb]
-// in fp32 VALU.  Tiles of A and W are double-buffered in LDS with a
-// 144-byte row stride (conflict-free 16-byte operand reads); the next K
-// block's global loads are in flight during the current block's MFMAs.
+// v_mfma_f32_32x32x16_bf16, the weight as MFMA A operand and the activation
+// as B operand.
+//  * FP8 block scaling: each 128-deep K block is one MFMA chain started from
+//    zero (the MFMA's internal sum is not fp32-exact, so partial sums are
+//    promoted every 128 K), then acc += partial * sA[m, kb] * sW[n/128, kb]
+//    in fp32 VALU (one FMA per output per K block).
+//  * K loop: A and W tiles (128 rows x 128 bytes each step) double-buffered
+//    in LDS with a 144-byte row stride (conflict-free 16-byte operand
+//    reads); the next step's global loads are in flight during the current
+//    step's MFMAs; load addresses are fixed per thread outside the loop.
+//  * Epilogue through LDS: the fp32 tile is parked in LDS, then every row is
+//    finished by 16 consecutive threads (8 columns each): bias, residual,
+//    GELU and the per-row 128-column FP8 requant amax (16-lane shuffle)
+//    all happen there, and every global store is a full 16-byte run, so
+//    rows are written with whole cache lines.
+//  * Tile order is XCD-aware: workgroups are dealt round-robin to the 8
+//    XCDs, so block id b is remapped to a logical tile such that each XCD
+//    owns a contiguous range of M tiles (with all N tiles): each activation
+//    tile is fetched by one XCD's L2 only.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,6 +39,7 @@ constexpr int kBN = 128;   // output features per tile
 constexpr int kRowB = 128; // bytes of K per tile row per step
 constexpr int kLS = 144;   // LDS row stride in bytes
 constexpr int kTileB = 128 * kLS;
+constexpr int kCS = 132;   // fp32 row stride of the parked C tile (floats)
 }  // namespace
 
 __device__ __forceinline__ i32x8_t lds_read32(const uint8_t* p) {
@@ -42,44 +51,82 @@ __device__ __forceinline__ i32x8_t lds_read32(const uint8_t* p) {
   return r;
 }
 
+// Logical tile of this workgroup: XCD x = bid % 8 owns logical ids
+// [x*q + min(x, r), ...) where nblocks = 8q + r.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int x = bid & 7, i = bid >> 3;
+  return x * q + min(x, r) + i;
+}
+
+// Park the 64x64 fp32 accumulators of this wave in the LDS C tile (row = m
+// local, column = n local).
+__device__ __forceinline__ void park_acc(float* c_lds, const f32x16_t acc[2][2], int wn, int wm, int l32, int g) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int ml = 64 * wm + 32 * mt + l32;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int nl = 64 * wn + 32 * nt + 8 * rg + 4 * g;
+        *reinterpret_cast<float4*>(c_lds + ml * kCS + nl) =
+            make_float4(acc[nt][mt][4 * rg + 0], acc[nt][mt][4 * rg + 1], acc[nt][mt][4 * rg + 2],
+                        acc[nt][mt][4 * rg + 3]);
+      }
+    }
+  }
+}
+
 // ============================================================ FP8 block-128
 template <int EPI>
 __global__ __launch_bounds__(256) void fp8_gemm_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ a_scales, const uint8_t* __restrict__ w,
-    const float* __restrict__ w_scales, int M, int N, int Np, int Kp, int n_tiles,
+    const float* __restrict__ w_scales, int M, int N, int Np, int Kp, int n_tiles, int nblocks,
     const uint16_t* __restrict__ bias, const uint16_t* residual, uint16_t* out,
     uint8_t* __restrict__ out_codes, float* __restrict__ out_scales, float* __restrict__ prequant) {
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * kTileB];
-  __shared__ __attribute__((aligned(16))) uint8_t w_lds[2 * kTileB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileB];  // A x2, W x2; C tile after the loop
   __shared__ float sa_lds[2][kBM];
-  __shared__ float red[2][2][64];
+  uint8_t* a_lds = smem;
+  uint8_t* w_lds = smem + 2 * kTileB;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int l32 = lane & 31, g = lane >> 5;
-  const int n_tile = blockIdx.x % n_tiles, m_tile = blockIdx.x / n_tiles;
+  const int lb = xcd_logical_block(blockIdx.x, nblocks);
+  const int m_tile = lb / n_tiles, n_tile = lb % n_tiles;
   const int n0 = n_tile * kBN, m0 = m_tile * kBM;
   const int Kb = Kp >> 7;
 
-  uint4 ra[4], rw[4];
-  float rs = 0.0f;
+  // per-thread load slots: rows lrow + 32i, 16 bytes at lcol
   const int lrow = tid >> 3, lcol = (tid & 7) * 16;
+  uint32_t a_off[4], w_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a_off[i] = (uint32_t)(min(m0 + lrow + 32 * i, M - 1)) * (uint32_t)Kp + lcol;
+    w_off[i] = (uint32_t)(n0 + lrow + 32 * i) * (uint32_t)Kp + lcol;
+  }
+  const float* sa_ptr = a_scales + (size_t)min(m0 + (tid & 127), M - 1) * Kb;
+  const float* sw_ptr = w_scales + (size_t)n_tile * Kb;
+
+  u32x4_t ra[4], rw[4];
+  float rs = 0.0f;
   auto gload = [&](int kb) {
+    const uint8_t* ak = a + kb * kRowB;
+    const uint8_t* wk = w + kb * kRowB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = lrow + 32 * i;
-      const int am = min(m0 + row, M - 1);
-      ra[i] = *reinterpret_cast<const uint4*>(a + (int64_t)am * Kp + kb * kRowB + lcol);
-      rw[i] = *reinterpret_cast<const uint4*>(w + (int64_t)(n0 + row) * Kp + kb * kRowB + lcol);
+      ra[i] = *reinterpret_cast<const u32x4_t*>(ak + a_off[i]);
+      rw[i] = *reinterpret_cast<const u32x4_t*>(wk + w_off[i]);
     }
-    if (tid < kBM) rs = a_scales[(int64_t)min(m0 + tid, M - 1) * Kb + kb];
+    rs = sa_ptr[kb];
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = lrow + 32 * i;
-      *reinterpret_cast<uint4*>(a_lds + buf * kTileB + row * kLS + lcol) = ra[i];
-      *reinterpret_cast<uint4*>(w_lds + buf * kTileB + row * kLS + lcol) = rw[i];
+      *reinterpret_cast<u32x4_t*>(a_lds + buf * kTileB + row * kLS + lcol) = ra[i];
+      *reinterpret_cast<u32x4_t*>(w_lds + buf * kTileB + row * kLS + lcol) = rw[i];
     }
     if (tid < kBM) sa_lds[buf][tid] = rs;
   };
@@ -97,129 +144,122 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
   for (int kb = 0; kb < Kb; ++kb) {
     const int buf = kb & 1;
     if (kb + 1 < Kb) gload(kb + 1);
-    const float sw = w_scales[(int64_t)n_tile * Kb + kb];
-    const uint8_t* wl = w_lds + buf * kTileB;
-    const uint8_t* al = a_lds + buf * kTileB;
+    const float sw = sw_ptr[kb];
+    const uint8_t* wl = w_lds + buf * kTileB + (64 * wn + l32) * kLS + 32 * g;
+    const uint8_t* al = a_lds + buf * kTileB + (64 * wm + l32) * kLS + 32 * g;
     i32x8_t wop[2][2], aop[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        wop[t][kh] = lds_read32(wl + (64 * wn + 32 * t + l32) * kLS + 64 * kh + 32 * g);
-        aop[t][kh] = lds_read32(al + (64 * wm + 32 * t + l32) * kLS + 64 * kh + 32 * g);
+        wop[t][kh] = lds_read32(wl + 32 * t * kLS + 64 * kh);
+        aop[t][kh] = lds_read32(al + 32 * t * kLS + 64 * kh);
+      }
+    }
+    f32x16_t part[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        part[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[nt][0], aop[mt][0], f32x16_t{}, 0, 0,
+                                                                       0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        part[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[nt][1], aop[mt][1], part[nt][mt], 0,
+                                                                       0, 0, 0, 0, 0);
       }
     }
     float coef[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) coef[mt] = sa_lds[buf][64 * wm + 32 * mt + l32] * sw;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x16_t part = f32x16_t{};
-        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[nt][0], aop[mt][0], part, 0, 0, 0, 0, 0, 0);
-        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[nt][1], aop[mt][1], part, 0, 0, 0, 0, 0, 0);
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nt][mt][r] = fmaf(part[r], coef[mt], acc[nt][mt][r]);
-      }
-    }
+        for (int r = 0; r < 16; ++r) acc[nt][mt][r] = fmaf(part[nt][mt][r], coef[mt], acc[nt][mt][r]);
     if (kb + 1 < Kb) lstore(buf ^ 1);
     __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogue
-  // lane holds m = m0 + 64wm + 32mt + l32 and n = n0 + 64wn + 32nt + 8rg + 4g + j
-  if constexpr (EPI == 0 || EPI == 1) {
+  float* c_lds = reinterpret_cast<float*>(smem);
+  park_acc(c_lds, acc, wn, wm, l32, g);
+  __syncthreads();
+  // thread -> (row = tid/16 + 16 pass, 8 columns at (tid%16)*8)
+  const int cc = (tid & 15) * 8;
+  const int n = n0 + cc;
+  float b8[8];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int m = m0 + 64 * wm + 32 * mt + l32;
-      if (m >= M) continue;
+  for (int j = 0; j < 8; ++j) b8[j] = 0.0f;
+  if (bias) {
+    if (n + 8 <= N && (N & 7) == 0) {
+      load8_bf16(bias, n, N, b8);
+    } else {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int n = n0 + 64 * wn + 32 * nt + 8 * rg + 4 * g;
-          float y[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = acc[nt][mt][4 * rg + j];
-          if (n + 4 <= N && (N & 3) == 0) {
-            if (bias) {
-              const uint2 b = *reinterpret_cast<const uint2*>(bias + n);
-              y[0] += bf_lo(b.x); y[1] += bf_hi(b.x); y[2] += bf_lo(b.y); y[3] += bf_hi(b.y);
-            }
-            uint16_t* op = out + (int64_t)m * N + n;
-            if constexpr (EPI == 1) {
-              const uint2 rr = *reinterpret_cast<const uint2*>(residual + (int64_t)m * N + n);
-              y[0] += bf_lo(rr.x); y[1] += bf_hi(rr.x); y[2] += bf_lo(rr.y); y[3] += bf_hi(rr.y);
-            }
-            uint2 o2;
-            o2.x = pack_bf16x2(y[0], y[1]);
-            o2.y = pack_bf16x2(y[2], y[3]);
-            *reinterpret_cast<uint2*>(op) = o2;
+      for (int j = 0; j < 8; ++j) b8[j] = (n + j < N) ? bf2f(bias[n + j]) : 0.0f;
+    }
+  }
+#pragma unroll 2
+  for (int pass = 0; pass < 8; ++pass) {
+    const int ml = (tid >> 4) + 16 * pass;
+    const int m = m0 + ml;
+    const float4 c0 = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc);
+    const float4 c1 = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc + 4);
+    float y[8] = {c0.x + b8[0], c0.y + b8[1], c0.z + b8[2], c0.w + b8[3],
+                  c1.x + b8[4], c1.y + b8[5], c1.z + b8[6], c1.w + b8[7]};
+    if constexpr (EPI == 0 || EPI == 1) {
+      if (m < M) {
+        const bool vec = n + 8 <= N && (N & 7) == 0;
+        if constexpr (EPI == 1) {
+          float r8[8];
+          if (vec) {
+            load8_bf16(residual + (int64_t)m * N, n, N, r8);
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (n + j < N) {
-                float v = y[j] + (bias ? bf2f(bias[n + j]) : 0.0f);
-                if constexpr (EPI == 1) v += bf2f(residual[(int64_t)m * N + n + j]);
-                out[(int64_t)m * N + n + j] = f2bf(v);
-              }
-            }
+            for (int j = 0; j < 8; ++j) r8[j] = (n + j < N) ? bf2f(residual[(int64_t)m * N + n + j]) : 0.0f;
           }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y[j] += r8[j];
+        }
+        if (vec) {
+          uint4 o;
+          o.x = pack_bf16x2(y[0], y[1]);
+          o.y = pack_bf16x2(y[2], y[3]);
+          o.z = pack_bf16x2(y[4], y[5]);
+          o.w = pack_bf16x2(y[6], y[7]);
+          *reinterpret_cast<uint4*>(out + (int64_t)m * N + n) = o;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (n + j < N) out[(int64_t)m * N + n + j] = f2bf(y[j]);
         }
       }
-    }
-  } else {
-    // bias + GELU, then FP8 requant per row and 128 columns (= this n tile)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int n = n0 + 64 * wn + 32 * nt + 8 * rg + 4 * g;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float b = (bias && n + j < N) ? bf2f(bias[n + j]) : 0.0f;
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const float v = acc[nt][mt][4 * rg + j] + b;
-            acc[nt][mt][4 * rg + j] = (n + j < N) ? gelu_tanh(v) : 0.0f;
-          }
-        }
-      }
-    }
-    float amax[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    } else {
+      // GELU, then FP8 requant of this row's 128 columns (16 lanes x 8)
       float am = 0.0f;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(acc[nt][mt][r]));
-      am = fmaxf(am, __shfl_xor(am, 32));
-      if (g == 0) red[wm][wn][32 * mt + l32] = am;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) amax[mt] = fmaxf(red[wm][0][32 * mt + l32], red[wm][1][32 * mt + l32]);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int m = m0 + 64 * wm + 32 * mt + l32;
-      if (m >= M) continue;
+      for (int j = 0; j < 8; ++j) {
+        y[j] = (n + j < N) ? gelu_tanh(y[j]) : 0.0f;
+        am = fmaxf(am, fabsf(y[j]));
+      }
+      am = group16_max(am);
       float s, inv;
-      block_scale(amax[mt], s, inv);
-      if (wn == 0 && g == 0) out_scales[(int64_t)m * (Np >> 7) + n_tile] = s;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int n = n0 + 64 * wn + 32 * nt + 8 * rg + 4 * g;
-          const float y[4] = {acc[nt][mt][4 * rg + 0], acc[nt][mt][4 * rg + 1], acc[nt][mt][4 * rg + 2],
-                              acc[nt][mt][4 * rg + 3]};
-          *reinterpret_cast<uint32_t*>(out_codes + (int64_t)m * Np + n) =
-              e4m3x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
-          if (prequant) {
-            *reinterpret_cast<float4*>(prequant + (int64_t)m * Np + n) = make_float4(y[0], y[1], y[2], y[3]);
-          }
+      block_scale(am, s, inv);
+      if (m < M) {
+        uint2 cw;
+        cw.x = e4m3x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
+        cw.y = e4m3x4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
+        *reinterpret_cast<uint2*>(out_codes + (int64_t)m * Np + n) = cw;
+        if ((tid & 15) == 0) out_scales[(int64_t)m * (Np >> 7) + n_tile] = s;
+        if (prequant) {
+          float4* p = reinterpret_cast<float4*>(prequant + (int64_t)m * Np + n);
+          p[0] = make_float4(y[0], y[1], y[2], y[3]);
+          p[1] = make_float4(y[4], y[5], y[6], y[7]);
         }
       }
     }
@@ -235,19 +275,20 @@ hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_scales, const uint8_
   const int Kp = (K + 127) / 128 * 128;
   const int Np = (N + 127) / 128 * 128;
   const int n_tiles = Np / kBN, m_tiles = (M + kBM - 1) / kBM;
-  const dim3 grid(n_tiles * m_tiles);
+  const int nblocks = n_tiles * m_tiles;
+  const dim3 grid(nblocks);
   switch (epilogue) {
     case 0:
-      fp8_gemm_kernel<0><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, bias,
-                                                   residual, out, out_codes, out_scales, prequant);
+      fp8_gemm_kernel<0><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks,
+                                                   bias, residual, out, out_codes, out_scales, prequant);
       break;
     case 1:
-      fp8_gemm_kernel<1><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, bias,
-                                                   residual, out, out_codes, out_scales, prequant);
+      fp8_gemm_kernel<1><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks,
+                                                   bias, residual, out, out_codes, out_scales, prequant);
       break;
     case 2:
-      fp8_gemm_kernel<2><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, bias,
-                                                   residual, out, out_codes, out_scales, prequant);
+      fp8_gemm_kernel<2><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks,
+                                                   bias, residual, out, out_codes, out_scales, prequant);
       break;
     default:
       return hipErrorInvalidValue;
@@ -262,74 +303,78 @@ hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_scales, const uint8_
 template <int EPI, bool A_F32>
 __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__ a_ptr,
                                                         const uint16_t* __restrict__ w, int M, int N,
-                                                        int K, int n_tiles,
+                                                        int K, int n_tiles, int nblocks,
                                                         const uint16_t* __restrict__ bias,
                                                         const uint16_t* __restrict__ add,
                                                         uint16_t* __restrict__ out, int64_t ld_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * kTileB];
-  __shared__ __attribute__((aligned(16))) uint8_t w_lds[2 * kTileB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileB];
+  uint8_t* a_lds = smem;
+  uint8_t* w_lds = smem + 2 * kTileB;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int l32 = lane & 31, g = lane >> 5;
-  const int n_tile = blockIdx.x % n_tiles, m_tile = blockIdx.x / n_tiles;
+  const int lb = xcd_logical_block(blockIdx.x, nblocks);
+  const int m_tile = lb / n_tiles, n_tile = lb % n_tiles;
   const int n0 = n_tile * kBN, m0 = m_tile * kBM;
   const int ksteps = (K + 63) / 64;
 
   // bf16 A / W: chunk = 8 elements (16 B); row = tid/8 + 32i, col = (tid%8)*8
   // fp32 A: chunk = 4 elements (16 B in, 8 B out); row = tid/16 + 16i, col = (tid%16)*4
-  uint4 rw[4];
-  uint4 ra16[4];
-  float4 ra32[8];
+  const int wcol = (tid & 7) * 8;
+  uint32_t w_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w_off[i] = (uint32_t)min(n0 + (tid >> 3) + 32 * i, N - 1) * (uint32_t)K + wcol;
+  constexpr int NA = A_F32 ? 8 : 4;
+  const int acol = A_F32 ? (tid & 15) * 4 : (tid & 7) * 8;
+  uint32_t a_off[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = A_F32 ? (tid >> 4) + 16 * i : (tid >> 3) + 32 * i;
+    a_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + acol;
+  }
+
+  u32x4_t rw[4];
+  u32x4_t ra16[4];
+  f32x4_t ra32[8];
   auto gload = [&](int ks) {
     const int k0 = ks * 64;
+    const uint16_t* wk = w + k0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      const int kc = k0 + (tid & 7) * 8;
-      const int wr = min(n0 + row, N - 1);
-      rw[i] = kc < K ? *reinterpret_cast<const uint4*>(w + (int64_t)wr * K + kc) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      rw[i] = (k0 + wcol < K) ? *reinterpret_cast<const u32x4_t*>(wk + w_off[i]) : u32x4_t{0, 0, 0, 0};
     if constexpr (A_F32) {
-      const float* a = reinterpret_cast<const float*>(a_ptr);
+      const float* ak = reinterpret_cast<const float*>(a_ptr) + k0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = (tid >> 4) + 16 * i;
-        const int kc = k0 + (tid & 15) * 4;
-        const int ar = min(m0 + row, M - 1);
-        ra32[i] = kc < K ? *reinterpret_cast<const float4*>(a + (int64_t)ar * K + kc) : make_float4(0, 0, 0, 0);
-      }
+      for (int i = 0; i < 8; ++i)
+        ra32[i] = (k0 + acol < K) ? *reinterpret_cast<const f32x4_t*>(ak + a_off[i]) : f32x4_t{0, 0, 0, 0};
     } else {
-      const uint16_t* a = reinterpret_cast<const uint16_t*>(a_ptr);
+      const uint16_t* ak = reinterpret_cast<const uint16_t*>(a_ptr) + k0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 3) + 32 * i;
-        const int kc = k0 + (tid & 7) * 8;
-        const int ar = min(m0 + row, M - 1);
-        ra16[i] = kc < K ? *reinterpret_cast<const uint4*>(a + (int64_t)ar * K + kc) : make_uint4(0, 0, 0, 0);
-      }
+      for (int i = 0; i < 4; ++i)
+        ra16[i] = (k0 + acol < K) ? *reinterpret_cast<const u32x4_t*>(ak + a_off[i]) : u32x4_t{0, 0, 0, 0};
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(w_lds + buf * kTileB + row * kLS + (tid & 7) * 16) = rw[i];
+      *reinterpret_cast<u32x4_t*>(w_lds + buf * kTileB + row * kLS + (tid & 7) * 16) = rw[i];
     }
     if constexpr (A_F32) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = (tid >> 4) + 16 * i;
         uint2 p;
-        p.x = pack_bf16x2(ra32[i].x, ra32[i].y);
-        p.y = pack_bf16x2(ra32[i].z, ra32[i].w);
+        p.x = pack_bf16x2(ra32[i][0], ra32[i][1]);
+        p.y = pack_bf16x2(ra32[i][2], ra32[i][3]);
         *reinterpret_cast<uint2*>(a_lds + buf * kTileB + row * kLS + (tid & 15) * 8) = p;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = (tid >> 3) + 32 * i;
-        *reinterpret_cast<uint4*>(a_lds + buf * kTileB + row * kLS + (tid & 7) * 16) = ra16[i];
+        *reinterpret_cast<u32x4_t*>(a_lds + buf * kTileB + row * kLS + (tid & 7) * 16) = ra16[i];
       }
     }
   };
@@ -346,17 +391,15 @@ __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__
   for (int ks = 0; ks < ksteps; ++ks) {
     const int buf = ks & 1;
     if (ks + 1 < ksteps) gload(ks + 1);
-    const uint8_t* wl = w_lds + buf * kTileB;
-    const uint8_t* al = a_lds + buf * kTileB;
+    const uint8_t* wl = w_lds + buf * kTileB + (64 * wn + l32) * kLS + 16 * g;
+    const uint8_t* al = a_lds + buf * kTileB + (64 * wm + l32) * kLS + 16 * g;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8_t wop[2], aop[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        wop[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                  wl + (64 * wn + 32 * t + l32) * kLS + 32 * kk + 16 * g));
-        aop[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                  al + (64 * wm + 32 * t + l32) * kLS + 32 * kk + 16 * g));
+        wop[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wl + 32 * t * kLS + 32 * kk));
+        aop[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + 32 * t * kLS + 32 * kk));
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
@@ -368,25 +411,45 @@ __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__
     __syncthreads();
   }
 
+  float* c_lds = reinterpret_cast<float*>(smem);
+  park_acc(c_lds, acc, wn, wm, l32, g);
+  __syncthreads();
+  const int cc = (tid & 15) * 8;
+  const int n = n0 + cc;
+  float b8[8];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int m = m0 + 64 * wm + 32 * mt + l32;
+  for (int j = 0; j < 8; ++j) b8[j] = (bias && n + j < N) ? bf2f(bias[n + j]) : 0.0f;
+  const bool vec = n + 8 <= N && (N & 7) == 0 && (ld_out & 7) == 0;
+#pragma unroll 2
+  for (int pass = 0; pass < 8; ++pass) {
+    const int ml = (tid >> 4) + 16 * pass;
+    const int m = m0 + ml;
     if (m >= M) continue;
+    const float4 c0 = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc);
+    const float4 c1 = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc + 4);
+    float y[8] = {c0.x + b8[0], c0.y + b8[1], c0.z + b8[2], c0.w + b8[3],
+                  c1.x + b8[4], c1.y + b8[5], c1.z + b8[6], c1.w + b8[7]};
+    if constexpr (EPI == 1) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+      for (int j = 0; j < 8; ++j) y[j] = gelu_tanh(y[j]);
+    }
+    if constexpr (EPI == 2) {
+      if (add) {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int n = n0 + 64 * wn + 32 * nt + 8 * rg + 4 * g;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (n + j < N) {
-            float v = acc[nt][mt][4 * rg + j] + (bias ? bf2f(bias[n + j]) : 0.0f);
-            if constexpr (EPI == 1) v = gelu_tanh(v);
-            if constexpr (EPI == 2) v += add ? bf2f(add[(int64_t)m * N + n + j]) : 0.0f;
-            out[(int64_t)m * ld_out + n + j] = f2bf(v);
-          }
-        }
+        for (int j = 0; j < 8; ++j) y[j] += (n + j < N) ? bf2f(add[(int64_t)m * N + n + j]) : 0.0f;
       }
+    }
+    if (vec) {
+      uint4 o;
+      o.x = pack_bf16x2(y[0], y[1]);
+      o.y = pack_bf16x2(y[2], y[3]);
+      o.z = pack_bf16x2(y[4], y[5]);
+      o.w = pack_bf16x2(y[6], y[7]);
+      *reinterpret_cast<uint4*>(out + (int64_t)m * ld_out + n) = o;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (n + j < N) out[(int64_t)m * ld_out + n + j] = f2bf(y[j]);
     }
   }
 }
@@ -396,9 +459,10 @@ hipError_t launch_bf16_gemm(const void* a, bool a_f32, const uint16_t* w, int M,
                             uint16_t* out, int64_t ld_out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int n_tiles = (N + kBN - 1) / kBN, m_tiles = (M + kBM - 1) / kBM;
-  const dim3 grid(n_tiles * m_tiles);
-#define VIT_BG(E, F)                                                                                   \
-  bf16_gemm_kernel<E, F><<<grid, 256, 0, stream>>>(a, w, M, N, K, n_tiles, bias, add, out, ld_out)
+  const int nblocks = n_tiles * m_tiles;
+  const dim3 grid(nblocks);
+#define VIT_BG(E, F)                                                                                        \
+  bf16_gemm_kernel<E, F><<<grid, 256, 0, stream>>>(a, w, M, N, K, n_tiles, nblocks, bias, add, out, ld_out)
   if (a_f32) {
     switch (epilogue) {
       case 0: VIT_BG(0, true); break;
