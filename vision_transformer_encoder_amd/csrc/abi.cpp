@@ -153,7 +153,7 @@ hipError_t block_forward_impl(const vit_block_weights* w, uint16_t* x, int T, co
   if ((e = vit::launch_rope2d(ws.qkv, ws.qkv + H, 3 * H, pos, T, VIT_HEADS, VIT_HEAD_DIM, 10000.0f, s)) !=
       hipSuccess) return e;
   // attention
-  if ((e = launch_attention(ws.qkv, ws.qkv + H, ws.qkv + 2 * H, 3 * H, ws.o, H, cu_dev, num_seqs, q_tiles,
+  if ((e = launch_attention(ws.qkv, ws.qkv + H, ws.qkv + 2 * H, 3 * H, ws.o, H, cu_dev, num_seqs, T, q_tiles,
                             VIT_HEADS, 1.0f / std::sqrt((float)VIT_HEAD_DIM), s)) != hipSuccess) return e;
   // proj: x = bf16(x + Q(o) W^T + b)
   if ((e = vit::launch_quant_rows(ws.o, H, T, H, ws.a_codes, ws.a_scales, s)) != hipSuccess) return e;
@@ -360,8 +360,8 @@ int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64
   if (overlap(o, ob, q, ib) || overlap(o, ob, k, ib) || overlap(o, ob, v, ib)) return VIT_ERR_ALIAS;
   const int tiles = vit::attention_q_tiles(cu_seqlens_host, num_seqs);
   if ((int64_t)tiles * num_heads >= (int64_t)1 << 31) return VIT_ERR_SHAPE;
-  return hip_status(launch_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, num_seqs, tiles, num_heads,
-                                     softmax_scale, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, num_seqs, total_tokens, tiles,
+                                     num_heads, softmax_scale, static_cast<hipStream_t>(stream)));
 }
 
 int vit_merge2x2_layernorm(const uint16_t* x, int D, const int32_t* grid_hw_dev, const int32_t* grid_hw_host,

@@ -32,7 +32,7 @@ hipError_t launch_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* po
 
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             int64_t ld_qkv, uint16_t* o, int64_t ld_o, const int32_t* cu,
-                            int num_seqs, int total_q_tiles, int heads, float scale,
+                            int num_seqs, int total_tokens, int total_q_tiles, int heads, float scale,
                             hipStream_t stream);
 // Number of 128-query tiles the attention launch needs for these windows.
 int attention_q_tiles(const int32_t* cu_host, int num_seqs);
