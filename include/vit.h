@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define VIT_ABI_VERSION 1
+#define VIT_ABI_VERSION 2
 
 /* Model dimensions (FlashRT section 3; spark_model struct VisionEncoder). */
 #define VIT_HIDDEN 1152
@@ -196,12 +196,20 @@ int vit_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* pos_rc, int 
  * sizing only); cu[0] = 0, non-decreasing, cu[num_seqs] = total_tokens.
  * head_dim must be 72 (VIT_ERR_UNSUPPORTED otherwise); ld_qkv, ld_o % 8 == 0;
  * total_tokens * ld_qkv < 2^31.
+ * workspace: >= vit_attention_workspace_size() bytes of device memory,
+ * 16-byte aligned, not overlapping q, k, v or o (VIT_ERR_WORKSPACE if
+ * missing or too small).  It holds fp32 partial results of (window, head,
+ * 128-query) items whose key range is split between workgroups; its
+ * contents on entry do not matter.  Two calls in flight at once (on
+ * different streams) need different workspaces.
  * ------------------------------------------------------------------- */
+size_t vit_attention_workspace_size(void);
 int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
                   uint16_t* o, int64_t ld_o,
                   const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                   int num_seqs, int total_tokens, int num_heads, int head_dim,
-                  float softmax_scale, vit_stream_t stream);
+                  float softmax_scale, void* workspace, size_t workspace_bytes,
+                  vit_stream_t stream);
 
 /* ---------------------------------------------------------------------
  * 2x2 spatial merge fused with the merger LayerNorm (FlashRT section 3

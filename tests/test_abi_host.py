@@ -17,6 +17,7 @@ B = A + (1 << 30)
 C = A + (2 << 30)
 D = A + (3 << 30)
 E = A + (4 << 30)
+F = A + (5 << 30)
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +36,10 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.vit_abi_version() == 1
+    import re
+    hdr = open(vit.header_path).read()
+    declared = int(re.search(r"#define VIT_ABI_VERSION (\d+)", hdr).group(1))
+    assert lib.vit_abi_version() == declared == vit.ABI_VERSION
     for s in range(9):
         assert lib.vit_status_string(s)
     assert lib.vit_status_string(0) == b"ok"
@@ -105,20 +109,32 @@ def test_rope_validation(lib):
 
 def test_attention_validation(lib):
     f = lib.vit_attention
+    lib.vit_attention_workspace_size.restype = ctypes.c_size_t
+    wsb = lib.vit_attention_workspace_size()
+    assert wsb > 0 and wsb % 256 == 0
     cu = _cu([0, 5, 9])
     bad = _cu([1, 5, 9])
     dec = _cu([0, 6, 5])
-    args = lambda cuh, ns, T, hd=72, o=D: f(A, A + 2304, A + 4608, 3456, o, 1152, E, cuh, ns, T, 16, hd, 0.1, None)
-    assert args(cu, 2, 9, hd=64) == UNSUP
-    assert args(bad, 2, 9) == SEQ
-    assert args(dec, 2, 5) == SEQ
-    assert args(cu, 2, 10) == SEQ                 # last offset != total
-    assert args(cu, 2, 9, o=A + 64) == ALIAS      # output inside qkv
-    assert f(A, A + 2304, A + 4608, 3456, D, 1152, E, None, 2, 9, 16, 72, 0.1, None) == NULL
-    assert f(A, A + 2304, A + 4608, 3456, D, 1152, E, cu, 2, 9, 16, 72, 0.0, None) == SHAPE
-    assert f(A, A + 2304, A + 4608, 3452, D, 1152, E, cu, 2, 9, 16, 72, 0.1, None) == ALIGN
+
+    def call(q=A, ld=3456, o=D, cuh=cu, ns=2, T=9, hd=72, scale=0.1, ws=F, nb=None):
+        return f(q, q + 2304, q + 4608, ld, o, 1152, E, cuh, ns, T, 16, hd, ctypes.c_float(scale), ws,
+                 ctypes.c_size_t(wsb if nb is None else nb), None)
+
+    assert call(hd=64) == UNSUP
+    assert call(cuh=bad) == SEQ
+    assert call(cuh=dec, T=5) == SEQ
+    assert call(T=10) == SEQ                      # last offset != total
+    assert call(o=A + 64) == ALIAS                # output inside qkv
+    assert call(cuh=None) == NULL
+    assert call(scale=0.0) == SHAPE
+    assert call(ld=3452) == ALIGN
+    assert call(ws=None) == WS                    # workspace missing
+    assert call(nb=wsb - 1) == WS                 # workspace too small
+    assert call(ws=F + 8) == ALIGN                # workspace misaligned
+    assert call(ws=A) == ALIAS                    # workspace over qkv
+    assert call(ws=D - 16) == ALIAS               # workspace running into the output
     empty = _cu([0])
-    assert f(A, A + 2304, A + 4608, 3456, D, 1152, E, empty, 0, 0, 16, 72, 0.1, None) == OK
+    assert call(cuh=empty, ns=0, T=0, ws=None) == OK
 
 
 def test_merge_validation_statuses(lib):

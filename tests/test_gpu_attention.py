@@ -87,7 +87,10 @@ def test_attention_window_edge_cases(gpu):
     assert np.array_equal(o[0], v[0])
 
 
-def test_attention_packed_equals_separate_bitwise(gpu):
+def test_attention_packed_equals_separate(gpu):
+    """Windows packed in one call give what separate calls give.  The
+    stream-K split of the key ranges depends on the whole packing, so the
+    two agree to the attention tolerance rather than bit for bit."""
     grids = [(18, 54), (24, 76)]
     T, qkv, _, _, _ = _attention_case(gpu, grids)
     cu = synth.cu_seqlens(grids)
@@ -96,8 +99,8 @@ def test_attention_packed_equals_separate_bitwise(gpu):
     first = vit.vit_attention(qkv[:a, :1152], qkv[:a, 1152:2304], qkv[:a, 2304:], [0, a])
     second_qkv = qkv[a:].clone()
     second = vit.vit_attention(second_qkv[:, :1152], second_qkv[:, 1152:2304], second_qkv[:, 2304:], [0, T - a])
-    assert torch.equal(packed[:a].view(torch.int16), first.view(torch.int16))
-    assert torch.equal(packed[a:].view(torch.int16), second.view(torch.int16))
+    sep = torch.cat([first, second])
+    assert_close(host_f64(packed), host_f64(sep), 1e-2, 0.99999, "packed vs separate")
 
 
 def test_attention_constant_v_and_deterministic(gpu):

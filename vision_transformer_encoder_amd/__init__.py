@@ -24,7 +24,7 @@ __all__ = [
     "VitError", "require_library", "library_path", "declared_functions",
     "vit_abi_version", "vit_status_string", "vit_quant_fp8_block128", "vit_e4m3_encode",
     "vit_layernorm_quant_fp8", "vit_fp8_block128_gemm", "vit_bf16_gemm", "vit_rope2d",
-    "vit_attention", "vit_merge2x2_layernorm", "vit_block_workspace_size", "vit_block_forward",
+    "vit_attention", "vit_attention_workspace_size", "vit_merge2x2_layernorm", "vit_block_workspace_size", "vit_block_forward",
     "vit_encoder_workspace_size", "vit_encoder_forward", "BlockWeights", "MergerWeights",
     "EncoderWeights", "EPI_BIAS", "EPI_BIAS_RESIDUAL", "EPI_BIAS_GELU_FP8", "BEPI_BIAS",
     "BEPI_BIAS_GELU", "BEPI_BIAS_ADD",
@@ -35,6 +35,7 @@ _ROOT = os.path.dirname(_PKG)
 library_path = os.path.join(_PKG, "libvit.so")
 header_path = os.path.join(_ROOT, "include", "vit.h")
 
+ABI_VERSION = 2  # VIT_ABI_VERSION of the include/vit.h these signatures follow
 HIDDEN, HEADS, HEAD_DIM, MLP, MLP_PADDED = 1152, 16, 72, 4304, 4352
 PATCH_DIM, DEPTH, OUT_HIDDEN, MERGED_DIM, NUM_TAPS = 1536, 27, 4096, 4608, 4
 EPI_BIAS, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_FP8 = 0, 1, 2
@@ -83,7 +84,8 @@ _SIGS = {
     "vit_fp8_block128_gemm": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
     "vit_bf16_gemm": (_I, [_P, _I, _P, _I, _I, _I, _P, _P, _I, _P, _I64, _P]),
     "vit_rope2d": (_I, [_P, _P, _I64, _P, _I, _I, _I, _F, _P]),
-    "vit_attention": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _P]),
+    "vit_attention_workspace_size": (_SZ, []),
+    "vit_attention": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "vit_merge2x2_layernorm": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, _F, _P, _P]),
     "vit_block_workspace_size": (_SZ, [_I]),
     "vit_block_forward": (_I, [ctypes.POINTER(_BlockW), _P, _I, _P, _P, _P, _I, _P, _SZ, _P]),
@@ -106,6 +108,9 @@ def require_library() -> ctypes.CDLL:
             f = getattr(lib, name)
             f.restype = res
             f.argtypes = args
+        if lib.vit_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{library_path} has ABI version {lib.vit_abi_version()}, this binding "
+                               f"expects {ABI_VERSION}: rebuild it")
         _lib = lib
     return _lib
 
@@ -246,7 +251,8 @@ def vit_rope2d(q: torch.Tensor, k: torch.Tensor, pos_rc: torch.Tensor, num_heads
 def vit_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Sequence[int],
                   cu_seqlens_dev: Optional[torch.Tensor] = None, num_heads: int = HEADS,
                   head_dim: int = HEAD_DIM, softmax_scale: Optional[float] = None,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     ld = _row_ld(q)
     if _row_ld(k) != ld or _row_ld(v) != ld:
         raise ValueError("q, k, v must share a row stride")
@@ -257,9 +263,16 @@ def vit_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens:
     if out is None:
         out = torch.empty((T, num_heads * head_dim), dtype=torch.bfloat16, device=q.device)
     scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
+    if workspace is None:
+        workspace = _workspace(vit_attention_workspace_size(), q.device)
     _call("vit_attention", _p(q), _p(k), _p(v), ld, _p(out), _row_ld(out), _p(cu_seqlens_dev), cu_ptr,
-          len(cu_h) - 1, T, num_heads, head_dim, scale, _stream(q.device))
+          len(cu_h) - 1, T, num_heads, head_dim, scale, _p(workspace), workspace.numel() * workspace.element_size(),
+          _stream(q.device))
     return out
+
+
+def vit_attention_workspace_size() -> int:
+    return int(require_library().vit_attention_workspace_size())
 
 
 def vit_merge2x2_layernorm(x: torch.Tensor, grids: Sequence[Tuple[int, int]], gamma: torch.Tensor,

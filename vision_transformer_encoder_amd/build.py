@@ -32,11 +32,15 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source additions.  attention.hip: every value its max reductions see is
+# finite (masked keys carry a large finite negative score), so the NaN
+# quieting that IEEE fmaxf otherwise needs before each v_max is dropped.
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-x", "hip", "-c",
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-Rpass-analysis=kernel-resource-usage", "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

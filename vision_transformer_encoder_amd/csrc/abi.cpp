@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <vector>
 #include <cstdint>
 
 #include "kernels.h"
@@ -55,6 +56,7 @@ inline bool valid_grids(const int32_t* g, int n, int T) {
 struct BlockWs {
   uint16_t* qkv;     // [T, 3456]
   uint16_t* o;       // [T, 1152]
+  float* attn_part;  // attention partials (attention_partial_bytes())
   uint8_t* a_codes;  // [T, 1152]
   float* a_scales;   // [T, 9]
   uint8_t* h_codes;  // [T, 4352]
@@ -73,6 +75,7 @@ BlockWs block_ws_layout(void* base, int T) {
   const size_t t = (size_t)T;
   w.qkv = static_cast<uint16_t*>(take(t * 3 * VIT_HIDDEN * 2));
   w.o = static_cast<uint16_t*>(take(t * VIT_HIDDEN * 2));
+  w.attn_part = static_cast<float*>(take(vit::attention_partial_bytes()));
   w.a_codes = static_cast<uint8_t*>(take(t * VIT_HIDDEN));
   w.a_scales = static_cast<float*>(take(t * (VIT_HIDDEN / 128) * 4));
   w.h_codes = static_cast<uint8_t*>(take(t * VIT_MLP_PADDED));
@@ -138,7 +141,7 @@ int check_merger_weights(const vit_merger_weights* m) {
 
 // ---------------------------------------------------------------- block
 hipError_t block_forward_impl(const vit_block_weights* w, uint16_t* x, int T, const int32_t* pos,
-                              const int32_t* cu_dev, int num_seqs, int q_tiles, const BlockWs& ws,
+                              const int32_t* cu_dev, int num_seqs, int64_t attn_work, const BlockWs& ws,
                               hipStream_t s) {
   constexpr int H = VIT_HIDDEN;
   hipError_t e;
@@ -153,8 +156,9 @@ hipError_t block_forward_impl(const vit_block_weights* w, uint16_t* x, int T, co
   if ((e = vit::launch_rope2d(ws.qkv, ws.qkv + H, 3 * H, pos, T, VIT_HEADS, VIT_HEAD_DIM, 10000.0f, s)) !=
       hipSuccess) return e;
   // attention
-  if ((e = launch_attention(ws.qkv, ws.qkv + H, ws.qkv + 2 * H, 3 * H, ws.o, H, cu_dev, num_seqs, T, q_tiles,
-                            VIT_HEADS, 1.0f / std::sqrt((float)VIT_HEAD_DIM), s)) != hipSuccess) return e;
+  if ((e = launch_attention(ws.qkv, ws.qkv + H, ws.qkv + 2 * H, 3 * H, ws.o, H, cu_dev, num_seqs, T, attn_work,
+                            VIT_HEADS, 1.0f / std::sqrt((float)VIT_HEAD_DIM), ws.attn_part, s)) != hipSuccess)
+    return e;
   // proj: x = bf16(x + Q(o) W^T + b)
   if ((e = vit::launch_quant_rows(ws.o, H, T, H, ws.a_codes, ws.a_scales, s)) != hipSuccess) return e;
   if ((e = vit::launch_fp8_gemm(ws.a_codes, ws.a_scales, w->proj_codes, w->proj_scales, T, H, H,
@@ -337,9 +341,12 @@ int vit_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* pos_rc, int 
                                        static_cast<hipStream_t>(stream)));
 }
 
+size_t vit_attention_workspace_size(void) { return vit::attention_partial_bytes(); }
+
 int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv, uint16_t* o,
                   int64_t ld_o, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
-                  int total_tokens, int num_heads, int head_dim, float softmax_scale, vit_stream_t stream) {
+                  int total_tokens, int num_heads, int head_dim, float softmax_scale, void* workspace,
+                  size_t workspace_bytes, vit_stream_t stream) {
   if (num_seqs < 0 || num_seqs > (1 << 20) || total_tokens < 0 || total_tokens > kMaxTokens || num_heads < 1 ||
       num_heads > 256)
     return VIT_ERR_SHAPE;
@@ -358,10 +365,16 @@ int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64
   const size_t ib = ((size_t)(total_tokens - 1) * ld_qkv + width) * 2;
   const size_t ob = ((size_t)(total_tokens - 1) * ld_o + width) * 2;
   if (overlap(o, ob, q, ib) || overlap(o, ob, k, ib) || overlap(o, ob, v, ib)) return VIT_ERR_ALIAS;
-  const int tiles = vit::attention_q_tiles(cu_seqlens_host, num_seqs);
-  if ((int64_t)tiles * num_heads >= (int64_t)1 << 31) return VIT_ERR_SHAPE;
-  return hip_status(launch_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, num_seqs, total_tokens, tiles,
-                                     num_heads, softmax_scale, static_cast<hipStream_t>(stream)));
+  const size_t wb = vit::attention_partial_bytes();
+  if (!workspace || workspace_bytes < wb) return VIT_ERR_WORKSPACE;
+  if (!al16(workspace)) return VIT_ERR_ALIGN;
+  if (overlap(workspace, wb, q, ib) || overlap(workspace, wb, k, ib) || overlap(workspace, wb, v, ib) ||
+      overlap(workspace, wb, o, ob))
+    return VIT_ERR_ALIAS;
+  const int64_t work = vit::attention_work_per_head(cu_seqlens_host, num_seqs);
+  return hip_status(launch_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, num_seqs, total_tokens, work,
+                                     num_heads, softmax_scale, static_cast<float*>(workspace),
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int vit_merge2x2_layernorm(const uint16_t* x, int D, const int32_t* grid_hw_dev, const int32_t* grid_hw_host,
@@ -403,8 +416,8 @@ int vit_block_forward(const vit_block_weights* w, uint16_t* x_inout, int T, cons
   if (overlap(workspace, ws.bytes, x_inout, (size_t)T * VIT_HIDDEN * 2) ||
       overlap(workspace, ws.bytes, pos_rc, (size_t)T * 8))
     return VIT_ERR_ALIAS;
-  const int tiles = vit::attention_q_tiles(cu_seqlens_host, num_seqs);
-  return hip_status(block_forward_impl(w, x_inout, T, pos_rc, cu_seqlens_dev, num_seqs, tiles, ws,
+  const int64_t work = vit::attention_work_per_head(cu_seqlens_host, num_seqs);
+  return hip_status(block_forward_impl(w, x_inout, T, pos_rc, cu_seqlens_dev, num_seqs, work, ws,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -447,9 +460,10 @@ int vit_encoder_forward(const vit_encoder_weights* w, const float* pixels, const
       overlap(last_hidden, last_hidden ? xb : 0, pos_embed, pos_embed ? xb : 0))
     return VIT_ERR_ALIAS;
 
-  // attention q tiles of the packing, from the host copy of the grids
-  int tiles = 0;
-  for (int j = 0; j < num_images; ++j) tiles += (grid_hw_host[2 * j] * grid_hw_host[2 * j + 1] + 127) / 128;
+  // attention work of the packing, from the host copy of the grids
+  std::vector<int32_t> cu_host(num_images + 1, 0);
+  for (int j = 0; j < num_images; ++j) cu_host[j + 1] = cu_host[j] + grid_hw_host[2 * j] * grid_hw_host[2 * j + 1];
+  const int64_t work = vit::attention_work_per_head(cu_host.data(), num_images);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint16_t* x = last_hidden ? last_hidden : ws.x;
@@ -462,7 +476,7 @@ int vit_encoder_forward(const vit_encoder_weights* w, const float* pixels, const
   int ti = 0;
   const size_t tap_elems = (size_t)(T / 4) * VIT_OUT_HIDDEN;
   for (int b = 0; b < VIT_DEPTH; ++b) {
-    if ((e = block_forward_impl(&w->blocks[b], x, T, ws.pos, ws.cu, num_images, tiles, ws.blk, s)) != hipSuccess)
+    if ((e = block_forward_impl(&w->blocks[b], x, T, ws.pos, ws.cu, num_images, work, ws.blk, s)) != hipSuccess)
       return VIT_ERR_HIP;
     if (ti < VIT_NUM_TAPS && b + 1 == taps[ti]) {
       if ((e = merger_forward_impl(&w->mergers[ti], x, grid_hw_dev, num_images, T, out + ti * tap_elems, ws, s)) !=

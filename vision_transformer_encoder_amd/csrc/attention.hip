@@ -38,6 +38,9 @@
 //  * Workgroup id -> (q tile, head) with head fastest: ids that share a head
 //    are congruent mod 8, so each XCD (ids round-robin over 8 XCDs) serves
 //    two heads and keeps their K/V in its own L2.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -170,68 +173,217 @@ __device__ __forceinline__ float halves_max(float x) {
   return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
 }
 
-__device__ __forceinline__ void mask_tile(f32x16_t s[2], int key0, int nkeys, int g) {
+// Softmax numerators of one S^T tile: P = exp2(S * scale - m) as the bf16
+// B operands of the PV MFMAs.
+__device__ __forceinline__ void exp_tile(bf16x8_t pb[2][2], const f32x16_t s[2], float scale_log2, float m) {
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int key = key0 + 32 * jt + 8 * (rr >> 2) + 4 * g + (rr & 3);
-      if (key >= nkeys) s[jt][rr] = -INFINITY;
+    for (int h = 0; h < 2; ++h) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[jt][8 * h + j], scale_log2, -m));
+      u32x4_t w;
+      w[0] = pack_bf16x2(p[0], p[1]);
+      w[1] = pack_bf16x2(p[2], p[3]);
+      w[2] = pack_bf16x2(p[4], p[5]);
+      w[3] = pack_bf16x2(p[6], p[7]);
+      pb[jt][h] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
 }
 
-__global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ q,
-                                                           const uint16_t* __restrict__ k,
-                                                           const uint16_t* __restrict__ v, int64_t ld,
-                                                           uint16_t* __restrict__ o, int64_t ldo,
-                                                           const int32_t* __restrict__ cu, int num_seqs,
-                                                           int heads, float scale_log2, int total) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks_mem[kStages * kKBuf];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_mem[kStages * kVBuf];
+// V^T fragment of PV MFMA i (i % 3 = row tile dt, i / 3 = 16-key slot).
+__device__ __forceinline__ bf16x8_t v_frag(const uint16_t* __restrict__ vt, int i, int l32, int g, int vrow2) {
+  const int dt = i % 3, ksl = i / 3;
+  const uint16_t* vr = vt + (dt < 2 ? 32 * dt + l32 : vrow2) * kVS + 4 * g + 16 * ksl;
+  const uint2 a0 = *reinterpret_cast<const uint2*>(vr);
+  const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 8);
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{a0.x, a0.y, a1.x, a1.y});
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
+// O^T += V^T P^T for one key tile (V^T stage `vt`), not interleaved.
+__device__ __forceinline__ void pv_tile(f32x16_t acc[3], const uint16_t* __restrict__ vt, const bf16x8_t pb[2][2],
+                                        int l32, int g, int vrow2) {
+#pragma unroll
+  for (int i = 0; i < 12; ++i)
+    acc[i % 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vt, i, l32, g, vrow2), pb[(i / 3) >> 1][(i / 3) & 1],
+                                                         acc[i % 3], 0, 0, 0);
+}
 
-  // ---- which (window, q tile, head)
-  const int head = blockIdx.x % heads;
-  int tile = blockIdx.x / heads;
-  int seq_begin = 0, seq_len = 0;
-  for (int s = 0; s < num_seqs; ++s) {
-    const int b = cu[s], e = cu[s + 1];
-    const int nt = (e - b + kBQ - 1) / kBQ;
-    if (tile < nt) {
-      seq_begin = b;
-      seq_len = e - b;
+// Scaled row max (log2 units) of one S^T tile: each lane owns one query.
+__device__ __forceinline__ float tile_max(const f32x16_t s[2], float scale_log2) {
+  float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+  for (int rr = 2; rr < 16; ++rr) {
+    a = fmaxf(a, s[0][rr]);
+    b = fmaxf(b, s[1][rr]);
+  }
+  return halves_max(fmaxf(a, b)) * scale_log2;
+}
+
+// The steady-state work of one key tile, interleaved by hand.  A wave issues
+// in order, so a long run of VALU work with no MFMA in it leaves the matrix
+// core idle; here every slot issues one MFMA followed by the VALU work that
+// fits under it:
+//   phase 1: the 10 MFMAs of S(j+1) = K(j+1) Q^T, each with 1-2 pairs of the
+//            exp2 of P(j);
+//   phase 2: the 12 MFMAs of O^T += V^T(j) P(j)^T, each with a share of the
+//            row max of S(j+1).
+// Consecutive MFMAs write different accumulators, LDS operand fragments are
+// read two MFMAs ahead, and sched_barrier keeps the compiler from regrouping
+// the slots.  Returns the scaled row max of S(j+1).
+__device__ __forceinline__ float tile_step(f32x16_t s_nxt[2], f32x16_t acc[3], const f32x16_t s_cur[2],
+                                           const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vt,
+                                           const bf16x8_t qf[5], float scale_log2, float m, int l32, int g,
+                                           int vrow2) {
+  // K fragment i: key half jt = i & 1, d chunk kc = i >> 1
+  const uint16_t* kr = ks + l32 * kKS + 8 * g;
+  auto k_frag = [&](int i) { return ld_bf16x8(kr + (i & 1) * 32 * kKS + 16 * (i >> 1)); };
+
+  u32x4_t pw[4];  // P(j) as bf16 pairs: pw[ksl] holds keys 16 ksl .. 16 ksl + 15
+  bf16x8_t kf[3];
+  kf[0] = k_frag(0);
+  kf[1] = k_frag(1);
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i + 2 < 10) kf[(i + 2) % 3] = k_frag(i + 2);
+    const int jt = i & 1, kc = i >> 1;
+    s_nxt[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[kc], kc == 0 ? f32x16_t{} : s_nxt[jt], 0, 0, 0);
+#pragma unroll
+    for (int e2 = 16 * i / 10; e2 < 16 * (i + 1) / 10; ++e2) {
+      const int e = 2 * e2, jc = e >> 4, rr = e & 15;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[jc][rr], scale_log2, -m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[jc][rr + 1], scale_log2, -m));
+      pw[e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  bf16x8_t vf[3];
+  vf[0] = v_frag(vt, 0, l32, g, vrow2);
+  vf[1] = v_frag(vt, 1, l32, g, vrow2);
+  float ma = -INFINITY, mb = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    if (i + 2 < 12) vf[(i + 2) % 3] = v_frag(vt, i + 2, l32, g, vrow2);
+    acc[i % 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], __builtin_bit_cast(bf16x8_t, pw[i / 3]),
+                                                         acc[i % 3], 0, 0, 0);
+#pragma unroll
+    for (int e = 32 * i / 12; e < 32 * (i + 1) / 12; ++e) {
+      if (e & 1)
+        mb = fmaxf(mb, s_nxt[e >> 4][e & 15]);
+      else
+        ma = fmaxf(ma, s_nxt[e >> 4][e & 15]);
+    }
+    // keep this slot's share of the max here (IR passes would otherwise
+    // sink the whole reduction past the last MFMA)
+    asm volatile("" : "+v"(ma), "+v"(mb));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return halves_max(fmaxf(ma, mb)) * scale_log2;
+}
+
+// Key masking costs no VALU work: Q carries 1.0 in padding column 72 and K
+// carries 0 there, except for the key rows of the last tile that lie past
+// the window, whose column 72 holds the most negative finite bf16.  Their
+// scores come out of the MFMA near -3.4e38 and their P underflows to 0.
+constexpr uint32_t kMaskedKey = 0xff7fu;  // bf16 -3.39e38
+
+// Partial result of a segment that does not cover its item's whole key
+// range: rows 0..71 unnormalised O^T, row 72 the row sum l, row 73 the
+// running max m (log2 units), 128 queries per row, fp32.
+constexpr int kSlotRows = kHD + 2;
+constexpr int kSlotFloats = kSlotRows * kBQ;
+constexpr int kMaxWorkgroups = 512;
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  const int32_t* cu;
+  float* partial;         // [2 * num_wgs][kSlotRows][kBQ]
+  int64_t ld, ldo;
+  int64_t work_per_head;  // sum over windows of (q tiles x key tiles)
+  int64_t work;           // work_per_head * heads
+  int num_seqs, heads, total, num_wgs;
+  float scale_log2;
+};
+
+// Work item = (head, window, q tile); its key tiles are the unit of work.
+// Items are ordered head-major, so the contiguous ranges that the XCD
+// mapping gives each XCD touch one or two heads' K/V.
+struct Segment {
+  int head, seq_begin, seq_len, qtile, kt, nk;  // kt: first key tile of the segment
+};
+
+__device__ __forceinline__ int64_t wg_start(const AttnParams& a, int g) { return (int64_t)g * a.work / a.num_wgs; }
+
+// Item and key tile at position p of the work order (p < work).
+__device__ Segment locate(const AttnParams& a, int64_t p) {
+  Segment s{};
+  s.head = (int)(p / a.work_per_head);
+  int64_t r = p - (int64_t)s.head * a.work_per_head;
+  for (int w = 0; w < a.num_seqs; ++w) {
+    const int b = a.cu[w], len = a.cu[w + 1] - b;
+    const int nq = (len + kBQ - 1) / kBQ, nk = (len + kBK - 1) / kBK;
+    const int64_t span = (int64_t)nq * nk;
+    if (r < span) {
+      s.seq_begin = b;
+      s.seq_len = len;
+      s.qtile = (int)(r / nk);
+      s.kt = (int)(r % nk);
+      s.nk = nk;
       break;
     }
-    tile -= nt;
+    r -= span;
   }
-  if (seq_len == 0) return;  // cannot happen for a correctly sized grid
+  return s;
+}
 
-  const int64_t hoff = (int64_t)head * kHD;
+// Key tiles [s.kt, kt_end) of one item: the pipelined flash loop.  With
+// slot == nullptr the segment covers the whole key range and writes the
+// normalised bf16 output, otherwise its partial (O, l, m) goes to slot.
+__device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& s, int kt_end, float* slot,
+                                            uint16_t* __restrict__ ks_mem, uint16_t* __restrict__ vt_mem) {
+  // an opaque copy of the thread id: addresses derived from it are rebuilt
+  // per segment instead of being hoisted out of the segment loop, where they
+  // would stay live in registers across the whole flash loop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const float scale_log2 = a.scale_log2;
+  const int64_t ld = a.ld;
+  const int64_t hoff = (int64_t)s.head * kHD;
+  const int ntiles = kt_end - s.kt;
+  const int row0 = s.seq_begin + s.kt * kBK;
+  const int last_valid = s.seq_len - (s.nk - 1) * kBK;  // valid keys in the window's last tile
 
-  // ---- constant parts of every stage (never overwritten): K padding columns
-  // 72..79 are zero; V^T row 72 is all ones, row 73 all zeros.
-  for (int i = tid; i < kStages * kBK; i += 256)
-    *reinterpret_cast<uint4*>(ks_mem + (i / kBK) * kKBuf + (i % kBK) * kKS + 72) = make_uint4(0, 0, 0, 0);
-  for (int i = tid; i < kStages * 2 * (kVS / 2); i += 256) {
-    const int st = i / kVS, rem = i % kVS;  // kVS dwords cover the two rows
-    const int row = 72 + rem / (kVS / 2), col = 2 * (rem % (kVS / 2));
-    *reinterpret_cast<uint32_t*>(vt_mem + st * kVBuf + row * kVS + col) = row == 72 ? 0x3f803f80u : 0u;
-  }
+  // the previous segment's readers of every stage are done past this point
+  __syncthreads();
+  // K padding columns 72..79 back to zero (a previous segment may have
+  // masked keys there); thread 64 st + r owns row r of stage st.
+  if (tid < kStages * kBK)
+    *reinterpret_cast<u32x4_t*>(ks_mem + (tid / kBK) * kKBuf + (tid % kBK) * kKS + 72) = u32x4_t{0, 0, 0, 0};
+  // mask the keys past the window in its last tile (global tile t in stage st)
+  auto mask_last = [&](int t, int st) {
+    if (t == s.nk - 1 && last_valid < kBK && tid >= kBK * st && tid < kBK * (st + 1) && tid - kBK * st >= last_valid)
+      *reinterpret_cast<uint32_t*>(ks_mem + st * kKBuf + (tid - kBK * st) * kKS + 72) = kMaskedKey;
+  };
 
-  // ---- Q^T operand: lane holds query q_row, d = 16kc + 8g .. +8 (zero past 72)
-  const int q_local = tile * kBQ + wave * 32 + l32;
-  const int q_row = min(q_local, seq_len - 1);
+  // ---- Q^T operand: lane holds query q_row, d = 16kc + 8g .. +8; d = 72 is
+  // the constant 1.0 that picks up the key mask, d = 73..79 are zero
+  const int q_local = s.qtile * kBQ + wave * 32 + l32;
+  const int q_row = min(q_local, s.seq_len - 1);
   bf16x8_t qf[5];
   {
-    const uint16_t* qp = q + (int64_t)(seq_begin + q_row) * ld + hoff;
+    const uint16_t* qp = a.q + (int64_t)(s.seq_begin + q_row) * ld + hoff;
 #pragma unroll
     for (int kc = 0; kc < 5; ++kc) {
       const int d = 16 * kc + 8 * g;
-      qf[kc] = d < kHD ? ld_bf16x8(qp + d) : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      qf[kc] = d < kHD ? ld_bf16x8(qp + d) : __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f80u, 0, 0, 0});
     }
   }
 
@@ -244,41 +396,27 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   for (int dt = 0; dt < 3; ++dt) acc[dt] = f32x16_t{};
   float m_run = -INFINITY;  // running max of scaled scores (log2 units)
 
-  const int ntiles = (seq_len + kBK - 1) / kBK;
+  // ---- prologue: the segment's tiles 0 and 1 into stages 0 and 1, tile 2
+  // into registers (loads past the window are harmless: see load_kv)
   const KVPlan plan = make_plan(tid, ld, hoff);
   KVRegs r;
-  load_kv(r, plan, k, v, ld, seq_begin, total, tid);
-  store_kv(r, plan, ks_mem, vt_mem, tid);
-  if (ntiles > 1) {
-    load_kv(r, plan, k, v, ld, seq_begin + kBK, total, tid);
-    store_kv(r, plan, ks_mem + kKBuf, vt_mem + kVBuf, tid);
+  {
+    KVRegs r1;
+    load_kv(r, plan, a.k, a.v, ld, row0, a.total, tid);
+    load_kv(r1, plan, a.k, a.v, ld, row0 + kBK, a.total, tid);
+    store_kv(r, plan, ks_mem, vt_mem, tid);
+    mask_last(s.kt, 0);
+    store_kv(r1, plan, ks_mem + kKBuf, vt_mem + kVBuf, tid);
+    mask_last(s.kt + 1, 1);
   }
+  load_kv(r, plan, a.k, a.v, ld, row0 + 2 * kBK, a.total, tid);
   __syncthreads();
 
   f32x16_t s_a[2], s_b[2];
   qk_tile(s_a, ks_mem, qf, l32, g);
-  if (seq_len < kBK) mask_tile(s_a, 0, seq_len, g);
+  float mx = tile_max(s_a, scale_log2);  // scaled row max of the current S tile
 
-  int bv = 0;  // stage holding tile it
-  // One key tile: softmax of s_cur (tile it) on the VALU while the MFMA unit
-  // computes s_nxt (tile it+1), then O += P V of tile it.
-  auto step = [&](int it, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2]) {
-    const int bk = bv == kStages - 1 ? 0 : bv + 1;  // stage of tile it+1
-    const int bw = bk == kStages - 1 ? 0 : bk + 1;  // stage for tile it+2
-    const bool more2 = it + 2 < ntiles;
-    if (more2) load_kv(r, plan, k, v, ld, seq_begin + (it + 2) * kBK, total, tid);
-
-    // ---- S(it+1) is queued on the MFMA unit first: it depends on nothing
-    // below and runs while the VALU does the softmax of S(it)
-    qk_tile(s_nxt, ks_mem + bk * kKBuf, qf, l32, g);
-
-    // ---- row max of S(it); lazy rescale of O
-    float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
-#pragma unroll
-    for (int rr = 2; rr < 16; ++rr) mx = fmaxf(mx, s_cur[0][rr]);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s_cur[1][rr]);
-    mx = halves_max(mx) * scale_log2;
+  auto rescale = [&]() {
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -286,63 +424,64 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 #pragma unroll
       for (int dt = 0; dt < 3; ++dt) acc[dt] *= alpha;
     }
+  };
 
-    // ---- P(it) = exp2(S * scale - m)
-    bf16x8_t pb[2][2];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[jt][8 * h + j], scale_log2, -m_run));
-        uint4 w;
-        w.x = pack_bf16x2(p[0], p[1]);
-        w.y = pack_bf16x2(p[2], p[3]);
-        w.z = pack_bf16x2(p[4], p[5]);
-        w.w = pack_bf16x2(p[6], p[7]);
-        pb[jt][h] = __builtin_bit_cast(bf16x8_t, w);
-      }
-    }
-
-    // ---- O^T += V^T P^T (tile it)
-    const uint16_t* vt = vt_mem + bv * kVBuf;
-#pragma unroll
-    for (int dt = 0; dt < 3; ++dt) {
-      const uint16_t* vr = vt + (dt < 2 ? 32 * dt + l32 : vrow2) * kVS + 4 * g;
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kb = 32 * jt + 16 * h;
-          const uint2 a0 = *reinterpret_cast<const uint2*>(vr + kb);
-          const uint2 a1 = *reinterpret_cast<const uint2*>(vr + kb + 8);
-          const uint4 w = make_uint4(a0.x, a0.y, a1.x, a1.y);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb[jt][h], acc[dt],
-                                                           0, 0, 0);
-        }
-      }
-    }
-
-    if ((it + 2) * kBK > seq_len && it + 1 < ntiles) mask_tile(s_nxt, (it + 1) * kBK, seq_len, g);
-    if (more2) store_kv(r, plan, ks_mem + bw * kKBuf, vt_mem + bw * kVBuf, tid);
+  int bv = 0;  // stage holding tile j
+  // Tile j (j < ntiles - 1).  Tile j+2 goes from registers to LDS and tile
+  // j+3 is fetched (past the segment these are harmless extra loads into a
+  // free stage).  Then the interleaved MFMA/VALU work of the tile.
+  auto body = [&](int j, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2]) {
+    const int bk = bv == kStages - 1 ? 0 : bv + 1;  // stage of tile j+1
+    const int bw = bk == kStages - 1 ? 0 : bk + 1;  // stage for tile j+2
+    rescale();
+    store_kv(r, plan, ks_mem + bw * kKBuf, vt_mem + bw * kVBuf, tid);
+    mask_last(s.kt + j + 2, bw);
+    load_kv(r, plan, a.k, a.v, ld, row0 + (j + 3) * kBK, a.total, tid);
+    mx = tile_step(s_nxt, acc, s_cur, ks_mem + bk * kKBuf, vt_mem + bv * kVBuf, qf, scale_log2, m_run, l32, g,
+                   vrow2);
     __syncthreads();
     bv = bk;
   };
+  // Last tile: P and PV only.
+  auto tail = [&](f32x16_t (&s_cur)[2]) {
+    rescale();
+    bf16x8_t pb[2][2];
+    exp_tile(pb, s_cur, scale_log2, m_run);
+    pv_tile(acc, vt_mem + bv * kVBuf, pb, l32, g, vrow2);
+  };
 
   // two tiles per trip with the S registers swapping roles: no copies
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, s_a, s_b);
-    if (it + 1 < ntiles) step(it + 1, s_b, s_a);
+  int j = 0;
+  for (; j + 2 < ntiles; j += 2) {
+    body(j, s_a, s_b);
+    body(j + 1, s_b, s_a);
+  }
+  if (j + 1 < ntiles) {
+    body(j, s_a, s_b);
+    tail(s_b);
+  } else {
+    tail(s_a);
   }
 
-  // ---- normalise and store: lane holds query q_local, d = 32dt + 8(rr/4) + 4g + rr%4;
-  // the row sum sits in acc[2][4] of the g == 0 half (row 72 of O^T).
-  const float l_lo = acc[2][4];
-  const float l_tot = __shfl(l_lo, l32);
+  // ---- results: lane holds query q_local, O^T rows d = 32dt + 8(rr/4) + 4g + rr%4;
+  // row 72 (the row sum) sits in acc[2][4] of the g == 0 half.
+  if (slot) {
+    const int qi = wave * 32 + l32;
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int d = 32 * dt + 8 * (rr >> 2) + 4 * g + (rr & 3);
+        if (d <= kHD) slot[d * kBQ + qi] = acc[dt][rr];
+      }
+    }
+    if (g == 0) slot[(kHD + 1) * kBQ + qi] = m_run;
+    return;
+  }
+  const float l_tot = __shfl(acc[2][4], l32);
   const float inv_l = 1.0f / l_tot;
-  if (q_local < seq_len) {
-    uint16_t* op = o + (int64_t)(seq_begin + q_local) * ldo + hoff;
+  if (q_local < s.seq_len) {
+    uint16_t* op = a.o + (int64_t)(s.seq_begin + q_local) * a.ldo + hoff;
 #pragma unroll
     for (int dt = 0; dt < 3; ++dt) {
 #pragma unroll
@@ -359,20 +498,137 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   }
 }
 
-int attention_q_tiles(const int32_t* cu_host, int num_seqs) {
-  int n = 0;
-  for (int s = 0; s < num_seqs; ++s) n += (cu_host[s + 1] - cu_host[s] + kBQ - 1) / kBQ;
+// Persistent stream-K grid: workgroup g (logical, XCD-grouped) takes the
+// key tiles [g W / G, (g+1) W / G) of the whole work order, so every
+// workgroup gets the same number of key tiles however the (window, q tile,
+// head) items divide into the resident slots.  Items cut by a range
+// boundary leave partials that attention_combine_kernel merges.
+__global__ __launch_bounds__(256, 2) void attention_kernel(AttnParams a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks_mem[kStages * kKBuf];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_mem[kStages * kVBuf];
+
+  // V^T row 72 is all ones, row 73 all zeros, in every stage (never overwritten)
+  for (int i = threadIdx.x; i < kStages * 2 * (kVS / 2); i += 256) {
+    const int st = i / kVS, rem = i % kVS;  // kVS dwords cover the two rows
+    const int row = 72 + rem / (kVS / 2), col = 2 * (rem % (kVS / 2));
+    *reinterpret_cast<uint32_t*>(vt_mem + st * kVBuf + row * kVS + col) = row == 72 ? 0x3f803f80u : 0u;
+  }
+
+  const int lg = xcd_logical_block(blockIdx.x, a.num_wgs);
+  int64_t p = wg_start(a, lg);
+  const int64_t end = wg_start(a, lg + 1);
+  while (p < end) {
+    const Segment s = locate(a, p);
+    if (s.nk == 0) break;  // only if the device windows disagree with the host's work count
+    const int kt_end = (int)min((int64_t)s.nk, s.kt + (end - p));
+    // a segment that starts inside its item uses slot 2g, one that starts
+    // the item but stops short of its end slot 2g + 1
+    float* slot = (s.kt == 0 && kt_end == s.nk) ? nullptr
+                                                : a.partial + (size_t)(2 * lg + (s.kt != 0 ? 0 : 1)) * kSlotFloats;
+    run_segment(a, s, kt_end, slot, ks_mem, vt_mem);
+    p += kt_end - s.kt;
+  }
+}
+
+// Merge the partials of every item that the stream-K ranges cut.  The
+// workgroup whose range holds an item's last key tile does it, reading the
+// item's segments in key order (deterministic):
+//   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  O = sum_s 2^(m_s - m) O_s / l.
+__global__ __launch_bounds__(256) void attention_combine_kernel(AttnParams a) {
+  const int lg = blockIdx.x;
+  const int64_t p = wg_start(a, lg), end = wg_start(a, lg + 1);
+  if (p >= end) return;
+  const Segment s = locate(a, p);
+  if (s.nk == 0 || s.kt == 0 || s.kt + (end - p) < s.nk) return;  // not an item's last segment
+  const int64_t p0 = p - s.kt;                        // the item's first key tile
+  int g0 = (int)(p0 * a.num_wgs / a.work);
+  while (g0 + 1 < a.num_wgs && wg_start(a, g0 + 1) <= p0) ++g0;
+  while (g0 > 0 && wg_start(a, g0) > p0) --g0;
+
+  const int tid = threadIdx.x, qi = tid & (kBQ - 1), half = tid / kBQ;
+  const int q_local = s.qtile * kBQ + qi;
+  if (q_local >= s.seq_len) return;
+  auto slot_of = [&](int gg) -> const float* {
+    return a.partial + (size_t)(gg == g0 ? 2 * gg + 1 : 2 * gg) * kSlotFloats;
+  };
+  float m = -INFINITY;
+  for (int gg = g0; gg <= lg; ++gg) m = fmaxf(m, slot_of(gg)[(kHD + 1) * kBQ + qi]);
+  constexpr int kHalf = kHD / 2;
+  float o[kHalf];
+#pragma unroll
+  for (int i = 0; i < kHalf; ++i) o[i] = 0.0f;
+  float l = 0.0f;
+  for (int gg = g0; gg <= lg; ++gg) {
+    const float* sl = slot_of(gg);
+    const float w = __builtin_amdgcn_exp2f(sl[(kHD + 1) * kBQ + qi] - m);
+    l = fmaf(w, sl[kHD * kBQ + qi], l);
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) o[i] = fmaf(w, sl[(half * kHalf + i) * kBQ + qi], o[i]);
+  }
+  const float inv_l = 1.0f / l;
+  uint16_t* op = a.o + (int64_t)(s.seq_begin + q_local) * a.ldo + (int64_t)s.head * kHD + half * kHalf;
+#pragma unroll
+  for (int i = 0; i < kHalf; i += 4) {
+    uint2 w;
+    w.x = pack_bf16x2(o[i] * inv_l, o[i + 1] * inv_l);
+    w.y = pack_bf16x2(o[i + 2] * inv_l, o[i + 3] * inv_l);
+    *reinterpret_cast<uint2*>(op + i) = w;
+  }
+}
+
+int64_t attention_work_per_head(const int32_t* cu_host, int num_seqs) {
+  int64_t n = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t len = cu_host[s + 1] - cu_host[s];
+    n += ((len + kBQ - 1) / kBQ) * ((len + kBK - 1) / kBK);
+  }
   return n;
 }
 
-hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                            int64_t ld_qkv, uint16_t* o, int64_t ld_o, const int32_t* cu,
-                            int num_seqs, int total_tokens, int total_q_tiles, int heads, float scale,
-                            hipStream_t stream) {
-  if (total_q_tiles == 0) return hipSuccess;
-  const float scale_log2 = scale * 1.4426950408889634f;
-  attention_kernel<<<total_q_tiles * heads, 256, 0, stream>>>(q, k, v, ld_qkv, o, ld_o, cu, num_seqs,
-                                                             heads, scale_log2, total_tokens);
+size_t attention_partial_bytes() { return (size_t)2 * kMaxWorkgroups * kSlotFloats * sizeof(float); }
+
+// Resident slots of the current device: two 256-thread workgroups per CU
+// (the kernel's register and LDS use allow two), at most kMaxWorkgroups.
+static int attention_slots() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxWorkgroups;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  const int slots = std::min(2 * cus, kMaxWorkgroups);
+  if (dev < 64) cache[dev].store(slots, std::memory_order_relaxed);
+  return slots;
+}
+
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv, uint16_t* o,
+                            int64_t ld_o, const int32_t* cu, int num_seqs, int total_tokens, int64_t work_per_head,
+                            int heads, float scale, float* partial, hipStream_t stream) {
+  if (work_per_head == 0) return hipSuccess;
+  AttnParams a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.cu = cu;
+  a.partial = partial;
+  a.ld = ld_qkv;
+  a.ldo = ld_o;
+  a.work_per_head = work_per_head;
+  a.work = work_per_head * heads;
+  a.num_seqs = num_seqs;
+  a.heads = heads;
+  a.total = total_tokens;
+  // every workgroup must own at least one key tile
+  a.num_wgs = (int)std::min<int64_t>(attention_slots(), a.work);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  attention_kernel<<<a.num_wgs, 256, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attention_combine_kernel<<<a.num_wgs, 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

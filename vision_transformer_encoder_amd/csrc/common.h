@@ -73,6 +73,16 @@ __device__ __forceinline__ float group16_max(float v) {
   return v;
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (id % 8).  Logical index
+// of workgroup `bid` such that XCD x owns the contiguous logical range
+// [x*q + min(x, r), ...), nblocks = 8q + r: neighbouring logical tiles share
+// an XCD and its L2.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int x = bid & 7, i = bid >> 3;
+  return x * q + min(x, r) + i;
+}
+
 // tanh-form GELU in fp32.
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)

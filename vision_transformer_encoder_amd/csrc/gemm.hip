@@ -51,14 +51,6 @@ __device__ __forceinline__ i32x8_t lds_read32(const uint8_t* p) {
   return r;
 }
 
-// Logical tile of this workgroup: XCD x = bid % 8 owns logical ids
-// [x*q + min(x, r), ...) where nblocks = 8q + r.
-__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
-  const int q = nblocks >> 3, r = nblocks & 7;
-  const int x = bid & 7, i = bid >> 3;
-  return x * q + min(x, r) + i;
-}
-
 // Park the 64x64 fp32 accumulators of this wave in the LDS C tile (row = m
 // local, column = n local).
 __device__ __forceinline__ void park_acc(float* c_lds, const f32x16_t acc[2][2], int wn, int wm, int l32, int g) {

@@ -30,12 +30,16 @@ hipError_t launch_bf16_gemm(const void* a, bool a_f32, const uint16_t* w, int M,
 hipError_t launch_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* pos, int T,
                          int heads, int head_dim, float theta, hipStream_t stream);
 
+// Stream-K attention: `partial` is device memory of attention_partial_bytes()
+// for the partials of items that the per-workgroup ranges cut; the launch
+// enqueues the main kernel and the combine kernel.
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             int64_t ld_qkv, uint16_t* o, int64_t ld_o, const int32_t* cu,
-                            int num_seqs, int total_tokens, int total_q_tiles, int heads, float scale,
-                            hipStream_t stream);
-// Number of 128-query tiles the attention launch needs for these windows.
-int attention_q_tiles(const int32_t* cu_host, int num_seqs);
+                            int num_seqs, int total_tokens, int64_t work_per_head, int heads,
+                            float scale, float* partial, hipStream_t stream);
+// Sum over windows of (128-query tiles x 64-key tiles).
+int64_t attention_work_per_head(const int32_t* cu_host, int num_seqs);
+size_t attention_partial_bytes();
 
 hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_hw,
                                   int num_images, int T, const uint16_t* gamma,
