@@ -48,7 +48,8 @@ namespace vit {
 
 namespace {
 constexpr int kHD = 72;
-constexpr int kBQ = 128;          // queries per workgroup
+constexpr int kThreads = 512;     // 8 waves
+constexpr int kBQ = 256;          // queries per workgroup: 32 per wave
 constexpr int kBK = 64;           // keys per tile
 constexpr int kKS = 88;           // K row stride in LDS (bf16): 80 used
 constexpr int kVS = 68;           // V^T row stride in LDS (bf16): 64 used
@@ -64,21 +65,24 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
 }
 
 // Staging of one K/V tile.  K: 64 rows x 9 chunks of 16 B = 576 chunks,
-// thread t owns chunks t, t+256 and (t < 64) t+512.  V: 16 groups of 4 keys
-// x 9 chunks of 8 d = 144 items (threads 0..143), 4 x 16 B each, transposed
-// into V^T on the way to LDS.  All offsets are fixed per thread.
-// V item mapping: lane group tid/16 picks the d chunk, tid%16 the key group,
+// thread t owns chunk t and (t < 64) chunk t+512.  V: 16 groups of 4 keys
+// x 9 chunks of 8 d = 144 items on threads 64..207 (v thread vt = t - 64),
+// 4 x 16 B each, transposed into V^T on the way to LDS.  All offsets are
+// fixed per thread.
+// V item mapping: lane group vt/16 picks the d chunk, vt%16 the key group,
 // with chunks ordered 0,2,1,3,4,6,5,7,8 so that the two 16-lane halves of
 // every 32-lane LDS write phase hit V^T rows 16 apart: with the 34-dword row
 // stride those are 32 banks apart, and each phase writes 64 distinct banks.
+constexpr int kVThread0 = 64;
+
 struct KVRegs {
-  u32x4_t k0, k1, k2;
+  u32x4_t k0, k1;
   u32x4_t v[4];
 };
 
 struct KVPlan {
-  uint32_t kgoff[3];  // byte offsets of the three K chunks within a tile
-  int klds[3];        // their LDS element offsets
+  uint32_t kgoff[2];  // byte offsets of the two K chunks within a tile
+  int klds[2];        // their LDS element offsets
   uint32_t vgoff;     // byte offset of key 4*vkg, chunk vc within a tile
   uint32_t vstride;   // bytes per row
   int vlds;           // V^T LDS offset of row 8*vc, column 4*vkg
@@ -87,18 +91,19 @@ struct KVPlan {
 __device__ __forceinline__ KVPlan make_plan(int tid, int64_t ld, int64_t hoff) {
   KVPlan p;
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < 2; ++i) {
     // 16 consecutive chunks = 16 consecutive rows of one column: the 16 lanes
     // of each ds_write_b128 phase hit distinct banks (44-dword row stride)
-    const int c = min(tid + 256 * i, 575);
+    const int c = min(tid + kThreads * i, 575);
     const int blk = c >> 4;
     const int row = (blk / 9) * 16 + (c & 15), col = blk % 9;
     p.kgoff[i] = (uint32_t)((row * ld + hoff + col * 8) * 2);
     p.klds[i] = row * kKS + col * 8;
   }
-  const int vgrp = min(tid >> 4, 8);
+  const int vt = min(max(tid - kVThread0, 0), 143);
+  const int vgrp = vt >> 4;
   const int vc = (vgrp == 1 || vgrp == 5) ? vgrp + 1 : ((vgrp == 2 || vgrp == 6) ? vgrp - 1 : vgrp);
-  const int vkg = tid & 15;
+  const int vkg = vt & 15;
   p.vgoff = (uint32_t)((4 * vkg * ld + hoff + vc * 8) * 2);
   p.vstride = (uint32_t)(ld * 2);
   p.vlds = 8 * vc * kVS + 4 * vkg;
@@ -123,9 +128,8 @@ __device__ __forceinline__ void load_kv(KVRegs& r, const KVPlan& p, const uint16
   const __amdgpu_buffer_rsrc_t kr = rows_rsrc(k, ld, row0, total);
   const __amdgpu_buffer_rsrc_t vr = rows_rsrc(v, ld, row0, total);
   r.k0 = buf_ld(kr, p.kgoff[0]);
-  r.k1 = buf_ld(kr, p.kgoff[1]);
-  if (tid < 64) r.k2 = buf_ld(kr, p.kgoff[2]);
-  if (tid < 144) {
+  if (tid < 576 - kThreads) r.k1 = buf_ld(kr, p.kgoff[1]);
+  if (tid >= kVThread0 && tid < kVThread0 + 144) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.v[i] = buf_ld(vr, p.vgoff + i * p.vstride);
   }
@@ -134,9 +138,8 @@ __device__ __forceinline__ void load_kv(KVRegs& r, const KVPlan& p, const uint16
 __device__ __forceinline__ void store_kv(const KVRegs& r, const KVPlan& p, uint16_t* __restrict__ ks,
                                          uint16_t* __restrict__ vt, int tid) {
   *reinterpret_cast<u32x4_t*>(ks + p.klds[0]) = r.k0;
-  *reinterpret_cast<u32x4_t*>(ks + p.klds[1]) = r.k1;
-  if (tid < 64) *reinterpret_cast<u32x4_t*>(ks + p.klds[2]) = r.k2;
-  if (tid < 144) {
+  if (tid < 576 - kThreads) *reinterpret_cast<u32x4_t*>(ks + p.klds[1]) = r.k1;
+  if (tid >= kVThread0 && tid < kVThread0 + 144) {
     // r.v[i] holds d = 8vc..8vc+7 of key 4vkg+i (dword j = d 8vc+2j, 8vc+2j+1);
     // write V^T[8vc+2j (+1)][4vkg .. 4vkg+3] with byte permutes.
 #pragma unroll
@@ -295,7 +298,7 @@ constexpr uint32_t kMaskedKey = 0xff7fu;  // bf16 -3.39e38
 // running max m (log2 units), 128 queries per row, fp32.
 constexpr int kSlotRows = kHD + 2;
 constexpr int kSlotFloats = kSlotRows * kBQ;
-constexpr int kMaxWorkgroups = 512;
+constexpr int kMaxWorkgroups = 256;
 
 struct AttnParams {
   const uint16_t* q;
@@ -503,12 +506,12 @@ __device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& 
 // workgroup gets the same number of key tiles however the (window, q tile,
 // head) items divide into the resident slots.  Items cut by a range
 // boundary leave partials that attention_combine_kernel merges.
-__global__ __launch_bounds__(256, 2) void attention_kernel(AttnParams a) {
+__global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams a) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_mem[kStages * kKBuf];
   __shared__ __attribute__((aligned(16))) uint16_t vt_mem[kStages * kVBuf];
 
   // V^T row 72 is all ones, row 73 all zeros, in every stage (never overwritten)
-  for (int i = threadIdx.x; i < kStages * 2 * (kVS / 2); i += 256) {
+  for (int i = threadIdx.x; i < kStages * 2 * (kVS / 2); i += kThreads) {
     const int st = i / kVS, rem = i % kVS;  // kVS dwords cover the two rows
     const int row = 72 + rem / (kVS / 2), col = 2 * (rem % (kVS / 2));
     *reinterpret_cast<uint32_t*>(vt_mem + st * kVBuf + row * kVS + col) = row == 72 ? 0x3f803f80u : 0u;
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnParams a) {
 // workgroup whose range holds an item's last key tile does it, reading the
 // item's segments in key order (deterministic):
 //   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  O = sum_s 2^(m_s - m) O_s / l.
-__global__ __launch_bounds__(256) void attention_combine_kernel(AttnParams a) {
+__global__ __launch_bounds__(2 * kBQ) void attention_combine_kernel(AttnParams a) {
   const int lg = blockIdx.x;
   const int64_t p = wg_start(a, lg), end = wg_start(a, lg + 1);
   if (p >= end) return;
@@ -587,8 +590,8 @@ int64_t attention_work_per_head(const int32_t* cu_host, int num_seqs) {
 
 size_t attention_partial_bytes() { return (size_t)2 * kMaxWorkgroups * kSlotFloats * sizeof(float); }
 
-// Resident slots of the current device: two 256-thread workgroups per CU
-// (the kernel's register and LDS use allow two), at most kMaxWorkgroups.
+// Resident slots of the current device: one 512-thread workgroup per CU,
+// at most kMaxWorkgroups.
 static int attention_slots() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -599,7 +602,7 @@ static int attention_slots() {
   }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  const int slots = std::min(2 * cus, kMaxWorkgroups);
+  const int slots = std::min(cus, kMaxWorkgroups);
   if (dev < 64) cache[dev].store(slots, std::memory_order_relaxed);
   return slots;
 }
@@ -625,10 +628,10 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   // every workgroup must own at least one key tile
   a.num_wgs = (int)std::min<int64_t>(attention_slots(), a.work);
   a.scale_log2 = scale * 1.4426950408889634f;
-  attention_kernel<<<a.num_wgs, 256, 0, stream>>>(a);
+  attention_kernel<<<a.num_wgs, kThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  attention_combine_kernel<<<a.num_wgs, 256, 0, stream>>>(a);
+  attention_combine_kernel<<<a.num_wgs, 2 * kBQ, 0, stream>>>(a);
   return hipGetLastError();
 }
 
