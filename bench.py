@@ -81,8 +81,9 @@ def encoder_flops(seq_lens, depth=27, n_mergers=4):
 
 
 def cpu_baseline(grids, cfg):
-    """Time the fp64 oracle on one block, the patch embed and one merger of
-    the workload and scale to the whole forward (27 blocks, 4 mergers)."""
+    """Time the fp64 oracle on two blocks, the patch embed and one merger of
+    the workload (about 14 s of CPU work at 6256 patches) and scale to the
+    whole forward (27 blocks, 4 mergers)."""
     import numpy as np
     import oracle as O
     import synth
@@ -101,17 +102,22 @@ def cpu_baseline(grids, cfg):
     pp = synth.patch_params(cfg)
     ew = O.EncoderWeights(patch_w=OI.dec(pp["patch_w"]), patch_b=OI.dec(pp["patch_b"]), blocks=[], mergers=[])
     px = synth.pixels(cfg, T).astype(np.float64)
+    bw2 = OI.block_weights(synth.block_params(cfg, 1))
+    for n in ("qkv", "proj", "fc1", "fc2"):
+        bw2.fp8(n)
     t0 = time.perf_counter()
     x = O.patch_embed(px, ew)
     t1 = time.perf_counter()
     x = O.block_forward(x, bw, pos, cu)
+    x = O.block_forward(x, bw2, pos, cu)
     t2 = time.perf_counter()
     O.merger_forward(x, mw, grids)
     t3 = time.perf_counter()
-    est_s = (t1 - t0) + 27 * (t2 - t1) + 4 * (t3 - t2)
+    per_block = (t2 - t1) / 2
+    est_s = (t1 - t0) + 27 * per_block + 4 * (t3 - t2)
     return {"value": est_s * 1e3 / len(grids), "unit": "ms/image", "cores": int(threads), "kind": "oracle",
-            "sample": f"patch embed + 1 of 27 blocks + 1 of 4 mergers at {T} patches "
-                      f"({t3 - t0:.1f} s measured: patch {t1 - t0:.2f} s, block {t2 - t1:.2f} s, "
+            "sample": f"patch embed + 2 of 27 blocks + 1 of 4 mergers at {T} patches "
+                      f"({t3 - t0:.1f} s measured: patch {t1 - t0:.2f} s, blocks {t2 - t1:.2f} s, "
                       f"merger {t3 - t2:.2f} s), scaled to 27 blocks + 4 mergers",
             "measured_s": round(t3 - t0, 2)}
 
@@ -174,16 +180,17 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
           file=sys.stderr, flush=True)
     ok = bool(torch.isfinite(out.float()).all().item())
@@ -193,7 +200,7 @@ def main() -> int:
     kernels = {}
     roofline = None
     if not args.no_kernels:
-        kernels = time_kernels(vit, W, T, grids, dev, args.kernel_reps, seq)
+        kernels = time_in_context(vit, W, px, grids, g_dev, dev, max(1, min(args.steps, 5)))
         a = kernels["attention"]
         roofline = {"bound": "mfma", "achieved": a["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(a["tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -209,6 +216,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"mean": round(ms_per_step, 4), "median": round(per_step_ms[len(per_step_ms) // 2], 4),
+                    "min": round(per_step_ms[0], 4)},
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -226,6 +235,8 @@ def main() -> int:
         line["kernels"] = kernels
         per_step = {k: v["us"] * v["per_step"] for k, v in kernels.items()}
         line["kernel_time_share"] = {k: round(v / (ms_per_step * 1e3), 3) for k, v in per_step.items()}
+        line["kernel_timing"] = ("average duration of each launch inside the running forward (the tower "
+                                 "run as its per-op C-ABI calls, HIP events on the launch stream)")
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(grids, cfg)
@@ -243,6 +254,100 @@ def _kernel_record(us, per_step, work, unit):
         peak = PEAK_FP8_TFLOPS if unit == "F8" else PEAK_BF16_TFLOPS
         r.update(flop=int(work), tflops=round(tf, 1), frac_mfma=round(tf / peak, 4))
     return r
+
+
+def kernel_work(T, seq):
+    """Algorithmic work of one launch of each kernel of the forward and how
+    many launches one forward makes: name -> (work, unit, per_step); unit
+    "B" = HBM bytes, "F8" / "F16" = FLOPs of an FP8 / bf16 MFMA kernel."""
+    H, B, TM = 1152, 27, T // 4
+    gemm = lambda n, k: 2 * T * n * k
+    return {
+        "layernorm_quant": (T * (H * 2 + H + 9 * 4), "B", 2 * B),
+        "fp8_gemm_qkv": (gemm(3 * H, H), "F8", B),
+        "rope2d": (T * 2 * H * 2 * 2 + T * 8, "B", B),
+        "attention": (sum(4 * p * p * H for p in seq), "F16", B),
+        "quant_rows": (T * (H * 2 + H + 9 * 4), "B", B),
+        "fp8_gemm_proj": (gemm(H, H), "F8", B),
+        "fp8_gemm_fc1_gelu_quant": (gemm(4304, H), "F8", B),
+        "fp8_gemm_fc2": (gemm(H, 4304), "F8", B),
+        "patch_embed_bf16": (gemm(H, 1536), "F16", 1),
+        "merge_layernorm": (2 * T * H * 2, "B", 4),
+        "merger_fc1_bf16": (2 * TM * 4608 * 4608, "F16", 4),
+        "merger_fc2_bf16": (2 * TM * 4096 * 4608, "F16", 4),
+    }
+
+
+def time_in_context(vit, W, px, grids, g_dev, dev, steps):
+    """Average duration of every kernel inside the running forward: the
+    tower is run as the sequence of per-op C-ABI calls vit_encoder_forward
+    makes (same kernels, shapes and order, on the same stream), with HIP
+    events recorded on that stream around every launch."""
+    import collections
+
+    import numpy as np
+    import torch
+
+    H = 1152
+    T = px.shape[0]
+    seq = [h * w for h, w in grids]
+    cu = np.concatenate([[0], np.cumsum(seq)]).astype(np.int32)
+    cu_dev = torch.from_numpy(cu).to(dev)
+    pos = torch.from_numpy(np.concatenate([np.stack(np.meshgrid(np.arange(h), np.arange(w), indexing="ij"), -1)
+                                           .reshape(-1, 2) for h, w in grids]).astype(np.int32)).to(dev)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    qkv = torch.empty((T, 3 * H), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    aws = torch.empty(vit.vit_attention_workspace_size(), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    spans = collections.defaultdict(list)
+
+    def timed(name, fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        r = fn()
+        e1.record(stream)
+        spans[name].append((e0, e1))
+        return r
+
+    taps = {8: 0, 16: 1, 24: 2, 27: 3}
+    for _ in range(steps):
+        timed("patch_embed_bf16", lambda: vit.vit_bf16_gemm(px, W.patch["patch_w"], bias=W.patch["patch_b"], out=x))
+        for b in range(27):
+            t, q = W.blocks[b].t, W.blocks[b].q
+            a_c, a_s = timed("layernorm_quant", lambda: vit.vit_layernorm_quant_fp8(x, t["ln1_g"], t["ln1_b"]))
+            timed("fp8_gemm_qkv", lambda: vit.vit_fp8_block128_gemm(a_c, a_s, q["qkv"][0], q["qkv"][1], 3 * H, H,
+                                                                    bias=t["qkv_b"], out=qkv))
+            timed("rope2d", lambda: vit.vit_rope2d(qkv[:, :H], qkv[:, H:2 * H], pos))
+            timed("attention", lambda: vit.vit_attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], cu,
+                                                         cu_seqlens_dev=cu_dev, out=o, workspace=aws))
+            o_c, o_s = timed("quant_rows", lambda: vit.vit_quant_fp8_block128(o))
+            timed("fp8_gemm_proj", lambda: vit.vit_fp8_block128_gemm(o_c, o_s, q["proj"][0], q["proj"][1], H, H,
+                                                                     bias=t["proj_b"], residual=x,
+                                                                     epilogue=vit.EPI_BIAS_RESIDUAL, out=x))
+            a_c, a_s = timed("layernorm_quant", lambda: vit.vit_layernorm_quant_fp8(x, t["ln2_g"], t["ln2_b"]))
+            h_c, h_s = timed("fp8_gemm_fc1_gelu_quant",
+                             lambda: vit.vit_fp8_block128_gemm(a_c, a_s, q["fc1"][0], q["fc1"][1], 4304, H,
+                                                               bias=t["fc1_b"], epilogue=vit.EPI_BIAS_GELU_FP8))
+            timed("fp8_gemm_fc2", lambda: vit.vit_fp8_block128_gemm(h_c, h_s, q["fc2"][0], q["fc2"][1], H, 4304,
+                                                                    bias=t["fc2_b"], residual=x,
+                                                                    epilogue=vit.EPI_BIAS_RESIDUAL, out=x))
+            if b + 1 in taps:
+                m = W.mergers[taps[b + 1]].t
+                y = timed("merge_layernorm",
+                          lambda: vit.vit_merge2x2_layernorm(x, grids, m["m_ln_g"], m["m_ln_b"], grid_dev=g_dev))
+                hh = timed("merger_fc1_bf16", lambda: vit.vit_bf16_gemm(y, m["m_fc1_w"], bias=m["m_fc1_b"],
+                                                                        epilogue=vit.BEPI_BIAS_GELU))
+                timed("merger_fc2_bf16", lambda: vit.vit_bf16_gemm(hh, m["m_fc2_w"], bias=m["m_fc2_b"]))
+    torch.cuda.synchronize()
+    work = kernel_work(T, seq)
+    res = {}
+    for name, sp in spans.items():
+        us = sum(e0.elapsed_time(e1) for e0, e1 in sp) * 1e3 / len(sp)
+        w, unit, per_step = work[name]
+        res[name] = _kernel_record(us, per_step, w, unit)
+        print(f"[bench] in forward: {name}: {res[name]}", file=sys.stderr, flush=True)
+    return res
 
 
 def time_kernels(vit, W, T, grids, dev, reps, seq, only=None, eager=False):

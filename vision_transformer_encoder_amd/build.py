@@ -9,6 +9,7 @@ Every call recompiles every source (no caching): objects go to
 from __future__ import annotations
 
 import concurrent.futures as cf
+import ctypes
 import os
 import re
 import shutil
@@ -74,6 +75,12 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # every symbol must resolve (a kernel whose host stub was not emitted
+    # links fine and only fails at load time)
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        raise RuntimeError(f"linked library does not load: {e}") from None
     shutil.move(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
