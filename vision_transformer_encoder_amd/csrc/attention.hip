@@ -5,13 +5,19 @@
 // of the tower and is compute-bound).
 //
 // gfx950 design (not the page's sm_120 kernel):
-//  * One 256-thread workgroup = 4 waves = 128 queries of one (window, head);
-//    each wave owns 32 queries for the whole key loop.
-//  * Everything is computed transposed, S^T = K Q^T and O^T = V^T P^T, with
+//  * Persistent stream-K grid: one 512-thread workgroup (8 waves, two per
+//    SIMD) per CU.  The unit of work is one 64-key tile of one work item
+//    (head, window, 256-query tile); the whole ordered list of key tiles is
+//    cut into equal contiguous ranges, one per workgroup, so the load is
+//    even whatever the window lengths.  An item cut by a range boundary
+//    leaves fp32 partials (O, l, m) that a small second kernel merges in key
+//    order, so the result does not depend on timing.
+//  * Each wave owns 32 queries of the item for its whole key range.
+//    Everything is computed transposed, S^T = K Q^T and O^T = V^T P^T, with
 //    v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane holds
 //    one column (lane % 32) and 16 rows, so every lane owns ONE query: the
 //    row max and the rescale of O stay in the lane's registers, plus one
-//    cross-half exchange (lane ^ 32) per tile.
+//    cross-half exchange (v_permlane32_swap) per tile.
 //  * P never leaves registers: the 16 key-rows a lane holds in S^T are, in
 //    order, the 8+8 k-slots of the B operand of two PV MFMAs (the key order
 //    inside an MFMA is a free permutation as long as V^T uses the same one).
@@ -19,25 +25,27 @@
 //    for V^T (3 row tiles of 32).  Of the third V^T tile, row 72 is all ones:
 //    its output row is the softmax denominator (sum of the bf16 P actually
 //    multiplied), accumulated and rescaled by the MFMA for free; rows 73..95
-//    are zero.  These rows come from registers, not LDS.
+//    are zero.  Q's padding column 72 is 1.0, which turns K's column 72 into
+//    an additive key mask inside the MFMA (no VALU masking).
 //  * Software pipeline across key tiles: while the VALU turns S(j) into P(j)
 //    (exp2 with the scale folded in), the MFMA unit already computes S(j+1);
-//    then the PV MFMAs of tile j run.  K and V^T tiles live in a 3-buffer LDS
-//    ring (tile j: V^T read, tile j+1: K read, tile j+2: being written), one
-//    barrier per tile; global loads of tile j+2 are in flight during tile j.
+//    then the PV MFMAs of tile j run, interleaved by hand with the row max
+//    of S(j+1).  K and V^T tiles live in a 3-buffer LDS ring (tile j: V^T
+//    read, tile j+1: K read, tile j+2: being written), one barrier per tile;
+//    global loads of tile j+3 are in flight during tile j.
 //  * The running max is only raised (and O rescaled) when a row max grows
 //    by more than 2^8 over it: exact after the final division by the row
 //    sum, and it removes the per-tile rescale of 48 accumulators.
 //  * Row strides in LDS (88 bf16 for K, 68 for V^T) keep the ds_read_b128 /
-//    ds_read_b64 operand fetches bank-conflict free.
+//    ds_read_b64 operand fetches and the staging writes bank-conflict free.
 //  * K/V tiles are fetched with buffer loads whose descriptor starts at the
 //    tile's first row and ends at the last token: per-thread offsets are
 //    fixed for the whole loop (no per-tile address arithmetic), and rows
 //    past the last token read as zero in hardware, so no clamping is needed
 //    (rows of the next window inside the batch are finite and masked).
-//  * Workgroup id -> (q tile, head) with head fastest: ids that share a head
-//    are congruent mod 8, so each XCD (ids round-robin over 8 XCDs) serves
-//    two heads and keeps their K/V in its own L2.
+//  * Items are ordered head-major and workgroup ids are mapped so that each
+//    XCD takes a contiguous run of ranges: an XCD's workgroups share one or
+//    two heads' K/V in its own L2.
 #include <algorithm>
 #include <atomic>
 
@@ -48,7 +56,8 @@ namespace vit {
 
 namespace {
 constexpr int kHD = 72;
-constexpr int kThreads = 512;     // 8 waves
+constexpr int kThreads = 512;     // 8 waves: two per SIMD (one wave per SIMD cannot overlap its
+                                  // own MFMA and VALU work well enough)
 constexpr int kBQ = 256;          // queries per workgroup: 32 per wave
 constexpr int kBK = 64;           // keys per tile
 constexpr int kKS = 88;           // K row stride in LDS (bf16): 80 used
@@ -58,6 +67,10 @@ constexpr int kVRows = kHD + 2;  // V^T rows 0..71, row 72 = ones, row 73 = zero
 constexpr int kVBuf = kVRows * kVS;
 constexpr int kStages = 3;
 constexpr float kLazy = 8.0f;     // rescale only when the max grows by > 2^8
+#ifndef VIT_ATTN_FRAG_AHEAD
+#define VIT_ATTN_FRAG_AHEAD 2
+#endif
+constexpr int kFragAhead = VIT_ATTN_FRAG_AHEAD;  // LDS operand fragments read this many MFMAs ahead
 }  // namespace
 
 __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
@@ -65,7 +78,7 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
 }
 
 // Staging of one K/V tile.  K: 64 rows x 9 chunks of 16 B = 576 chunks,
-// thread t owns chunk t and (t < 64) chunk t+512.  V: 16 groups of 4 keys
+// thread t owns chunks t, t + kThreads, ... (below 576).  V: 16 groups of 4 keys
 // x 9 chunks of 8 d = 144 items on threads 64..207 (v thread vt = t - 64),
 // 4 x 16 B each, transposed into V^T on the way to LDS.  All offsets are
 // fixed per thread.
@@ -75,14 +88,16 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
 // stride those are 32 banks apart, and each phase writes 64 distinct banks.
 constexpr int kVThread0 = 64;
 
+constexpr int kKChunks = (576 + kThreads - 1) / kThreads;  // K chunks per thread
+
 struct KVRegs {
-  u32x4_t k0, k1;
+  u32x4_t k[kKChunks];
   u32x4_t v[4];
 };
 
 struct KVPlan {
-  uint32_t kgoff[2];  // byte offsets of the two K chunks within a tile
-  int klds[2];        // their LDS element offsets
+  uint32_t kgoff[kKChunks];  // byte offsets of the K chunks within a tile
+  int klds[kKChunks];        // their LDS element offsets
   uint32_t vgoff;     // byte offset of key 4*vkg, chunk vc within a tile
   uint32_t vstride;   // bytes per row
   int vlds;           // V^T LDS offset of row 8*vc, column 4*vkg
@@ -91,7 +106,7 @@ struct KVPlan {
 __device__ __forceinline__ KVPlan make_plan(int tid, int64_t ld, int64_t hoff) {
   KVPlan p;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kKChunks; ++i) {
     // 16 consecutive chunks = 16 consecutive rows of one column: the 16 lanes
     // of each ds_write_b128 phase hit distinct banks (44-dword row stride)
     const int c = min(tid + kThreads * i, 575);
@@ -127,8 +142,9 @@ __device__ __forceinline__ void load_kv(KVRegs& r, const KVPlan& p, const uint16
                                         int tid) {
   const __amdgpu_buffer_rsrc_t kr = rows_rsrc(k, ld, row0, total);
   const __amdgpu_buffer_rsrc_t vr = rows_rsrc(v, ld, row0, total);
-  r.k0 = buf_ld(kr, p.kgoff[0]);
-  if (tid < 576 - kThreads) r.k1 = buf_ld(kr, p.kgoff[1]);
+#pragma unroll
+  for (int i = 0; i < kKChunks; ++i)
+    if (tid + kThreads * i < 576) r.k[i] = buf_ld(kr, p.kgoff[i]);
   if (tid >= kVThread0 && tid < kVThread0 + 144) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.v[i] = buf_ld(vr, p.vgoff + i * p.vstride);
@@ -137,8 +153,9 @@ __device__ __forceinline__ void load_kv(KVRegs& r, const KVPlan& p, const uint16
 
 __device__ __forceinline__ void store_kv(const KVRegs& r, const KVPlan& p, uint16_t* __restrict__ ks,
                                          uint16_t* __restrict__ vt, int tid) {
-  *reinterpret_cast<u32x4_t*>(ks + p.klds[0]) = r.k0;
-  if (tid < 576 - kThreads) *reinterpret_cast<u32x4_t*>(ks + p.klds[1]) = r.k1;
+#pragma unroll
+  for (int i = 0; i < kKChunks; ++i)
+    if (tid + kThreads * i < 576) *reinterpret_cast<u32x4_t*>(ks + p.klds[i]) = r.k[i];
   if (tid >= kVThread0 && tid < kVThread0 + 144) {
     // r.v[i] holds d = 8vc..8vc+7 of key 4vkg+i (dword j = d 8vc+2j, 8vc+2j+1);
     // write V^T[8vc+2j (+1)][4vkg .. 4vkg+3] with byte permutes.
@@ -245,14 +262,16 @@ __device__ __forceinline__ float tile_step(f32x16_t s_nxt[2], f32x16_t acc[3], c
   auto k_frag = [&](int i) { return ld_bf16x8(kr + (i & 1) * 32 * kKS + 16 * (i >> 1)); };
 
   u32x4_t pw[4];  // P(j) as bf16 pairs: pw[ksl] holds keys 16 ksl .. 16 ksl + 15
-  bf16x8_t kf[3];
-  kf[0] = k_frag(0);
-  kf[1] = k_frag(1);
+  constexpr int PF = kFragAhead;
+  bf16x8_t kf[PF + 1];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) kf[i] = k_frag(i);
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
-    if (i + 2 < 10) kf[(i + 2) % 3] = k_frag(i + 2);
+    if (i + PF < 10) kf[(i + PF) % (PF + 1)] = k_frag(i + PF);
     const int jt = i & 1, kc = i >> 1;
-    s_nxt[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[kc], kc == 0 ? f32x16_t{} : s_nxt[jt], 0, 0, 0);
+    s_nxt[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], qf[kc], kc == 0 ? f32x16_t{} : s_nxt[jt], 0,
+                                                        0, 0);
 #pragma unroll
     for (int e2 = 16 * i / 10; e2 < 16 * (i + 1) / 10; ++e2) {
       const int e = 2 * e2, jc = e >> 4, rr = e & 15;
@@ -263,14 +282,14 @@ __device__ __forceinline__ float tile_step(f32x16_t s_nxt[2], f32x16_t acc[3], c
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  bf16x8_t vf[3];
-  vf[0] = v_frag(vt, 0, l32, g, vrow2);
-  vf[1] = v_frag(vt, 1, l32, g, vrow2);
+  bf16x8_t vf[PF + 1];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) vf[i] = v_frag(vt, i, l32, g, vrow2);
   float ma = -INFINITY, mb = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 12; ++i) {
-    if (i + 2 < 12) vf[(i + 2) % 3] = v_frag(vt, i + 2, l32, g, vrow2);
-    acc[i % 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], __builtin_bit_cast(bf16x8_t, pw[i / 3]),
+    if (i + PF < 12) vf[(i + PF) % (PF + 1)] = v_frag(vt, i + PF, l32, g, vrow2);
+    acc[i % 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (PF + 1)], __builtin_bit_cast(bf16x8_t, pw[i / 3]),
                                                          acc[i % 3], 0, 0, 0);
 #pragma unroll
     for (int e = 32 * i / 12; e < 32 * (i + 1) / 12; ++e) {
@@ -295,7 +314,7 @@ constexpr uint32_t kMaskedKey = 0xff7fu;  // bf16 -3.39e38
 
 // Partial result of a segment that does not cover its item's whole key
 // range: rows 0..71 unnormalised O^T, row 72 the row sum l, row 73 the
-// running max m (log2 units), 128 queries per row, fp32.
+// running max m (log2 units), one column per query of the 256-query tile, fp32.
 constexpr int kSlotRows = kHD + 2;
 constexpr int kSlotFloats = kSlotRows * kBQ;
 constexpr int kMaxWorkgroups = 256;

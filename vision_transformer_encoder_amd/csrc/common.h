@@ -83,12 +83,17 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
   return x * q + min(x, r) + i;
 }
 
-// tanh-form GELU in fp32.
+// tanh-form GELU in fp32, evaluated through the identity
+// 0.5 x (1 + tanh(u)) = x / (1 + e^(-2u)),  u = sqrt(2/pi) (x + 0.044715 x^3):
+// one exp2 and one reciprocal instead of a tanh, and no cancellation in
+// 1 + tanh(u) for negative x (where that form loses most of its relative
+// precision).  e^(-2u) overflows to +inf for very negative x, giving -0.
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   const float k1 = 0.044715f;
-  float u = k0 * (x + k1 * x * x * x);
-  return 0.5f * x * (1.0f + tanhf(u));
+  const float u = k0 * (x + k1 * x * x * x);
+  const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);  // e^(-2u): -2 log2(e) u
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Load 8 bf16 starting at column c of a row as fp32; columns >= cols read 0.
