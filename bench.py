@@ -299,6 +299,16 @@ def time_in_context(vit, W, px, grids, g_dev, dev, steps):
     qkv = torch.empty((T, 3 * H), dtype=torch.bfloat16, device=dev)
     o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     aws = torch.empty(vit.vit_attention_workspace_size(), dtype=torch.uint8, device=dev)
+    # every intermediate is allocated once, as the C-ABI forward does: an
+    # allocation between two events could stall the host while the GPU idles
+    # between them
+    u8, f32 = torch.uint8, torch.float32
+    ln_q = (torch.empty((T, H), dtype=u8, device=dev), torch.empty((T, H // 128), dtype=f32, device=dev))
+    o_q = (torch.empty((T, H), dtype=u8, device=dev), torch.empty((T, H // 128), dtype=f32, device=dev))
+    h_q = (torch.empty((T, 4352), dtype=u8, device=dev), torch.empty((T, 4352 // 128), dtype=f32, device=dev))
+    y_m = torch.empty((T // 4, 4 * H), dtype=torch.bfloat16, device=dev)
+    h_m = torch.empty((T // 4, 4 * H), dtype=torch.bfloat16, device=dev)
+    z_m = torch.empty((T // 4, 4096), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
     spans = collections.defaultdict(list)
 
@@ -315,30 +325,32 @@ def time_in_context(vit, W, px, grids, g_dev, dev, steps):
         timed("patch_embed_bf16", lambda: vit.vit_bf16_gemm(px, W.patch["patch_w"], bias=W.patch["patch_b"], out=x))
         for b in range(27):
             t, q = W.blocks[b].t, W.blocks[b].q
-            a_c, a_s = timed("layernorm_quant", lambda: vit.vit_layernorm_quant_fp8(x, t["ln1_g"], t["ln1_b"]))
+            a_c, a_s = timed("layernorm_quant", lambda: vit.vit_layernorm_quant_fp8(x, t["ln1_g"], t["ln1_b"], out=ln_q))
             timed("fp8_gemm_qkv", lambda: vit.vit_fp8_block128_gemm(a_c, a_s, q["qkv"][0], q["qkv"][1], 3 * H, H,
                                                                     bias=t["qkv_b"], out=qkv))
             timed("rope2d", lambda: vit.vit_rope2d(qkv[:, :H], qkv[:, H:2 * H], pos))
             timed("attention", lambda: vit.vit_attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], cu,
                                                          cu_seqlens_dev=cu_dev, out=o, workspace=aws))
-            o_c, o_s = timed("quant_rows", lambda: vit.vit_quant_fp8_block128(o))
+            o_c, o_s = timed("quant_rows", lambda: vit.vit_quant_fp8_block128(o, out=o_q))
             timed("fp8_gemm_proj", lambda: vit.vit_fp8_block128_gemm(o_c, o_s, q["proj"][0], q["proj"][1], H, H,
                                                                      bias=t["proj_b"], residual=x,
                                                                      epilogue=vit.EPI_BIAS_RESIDUAL, out=x))
-            a_c, a_s = timed("layernorm_quant", lambda: vit.vit_layernorm_quant_fp8(x, t["ln2_g"], t["ln2_b"]))
+            a_c, a_s = timed("layernorm_quant", lambda: vit.vit_layernorm_quant_fp8(x, t["ln2_g"], t["ln2_b"], out=ln_q))
             h_c, h_s = timed("fp8_gemm_fc1_gelu_quant",
                              lambda: vit.vit_fp8_block128_gemm(a_c, a_s, q["fc1"][0], q["fc1"][1], 4304, H,
-                                                               bias=t["fc1_b"], epilogue=vit.EPI_BIAS_GELU_FP8))
+                                                               bias=t["fc1_b"], epilogue=vit.EPI_BIAS_GELU_FP8,
+                                                               out=h_q))
             timed("fp8_gemm_fc2", lambda: vit.vit_fp8_block128_gemm(h_c, h_s, q["fc2"][0], q["fc2"][1], H, 4304,
                                                                     bias=t["fc2_b"], residual=x,
                                                                     epilogue=vit.EPI_BIAS_RESIDUAL, out=x))
             if b + 1 in taps:
                 m = W.mergers[taps[b + 1]].t
                 y = timed("merge_layernorm",
-                          lambda: vit.vit_merge2x2_layernorm(x, grids, m["m_ln_g"], m["m_ln_b"], grid_dev=g_dev))
+                          lambda: vit.vit_merge2x2_layernorm(x, grids, m["m_ln_g"], m["m_ln_b"], grid_dev=g_dev,
+                                                             out=y_m))
                 hh = timed("merger_fc1_bf16", lambda: vit.vit_bf16_gemm(y, m["m_fc1_w"], bias=m["m_fc1_b"],
-                                                                        epilogue=vit.BEPI_BIAS_GELU))
-                timed("merger_fc2_bf16", lambda: vit.vit_bf16_gemm(hh, m["m_fc2_w"], bias=m["m_fc2_b"]))
+                                                                        epilogue=vit.BEPI_BIAS_GELU, out=h_m))
+                timed("merger_fc2_bf16", lambda: vit.vit_bf16_gemm(hh, m["m_fc2_w"], bias=m["m_fc2_b"], out=z_m))
     torch.cuda.synchronize()
     work = kernel_work(T, seq)
     res = {}

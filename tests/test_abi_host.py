@@ -207,3 +207,21 @@ def test_workspace_sizes_monotone(lib):
     assert sizes == sorted(sizes) and sizes[0] > 0
     assert lib.vit_block_workspace_size(-1) == 0
     assert lib.vit_encoder_workspace_size(6256, 1) > lib.vit_block_workspace_size(6256)
+
+
+def test_binding_rejects_mismatched_output_buffers():
+    # caller-provided outputs are checked for shape, dtype and contiguity
+    # before anything reaches the library
+    import torch
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    g = torch.ones(256, dtype=torch.bfloat16)
+    good_s = torch.empty((4, 2), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        vit.vit_layernorm_quant_fp8(x, g, g, out=(torch.empty((4, 128), dtype=torch.uint8), good_s))
+    with pytest.raises(ValueError):
+        vit.vit_layernorm_quant_fp8(x, g, g, out=(torch.empty((4, 256), dtype=torch.int8), good_s))
+    with pytest.raises(ValueError):
+        vit.vit_quant_fp8_block128(x, out=(torch.empty((4, 256), dtype=torch.uint8),
+                                           torch.empty((2, 4), dtype=torch.float32).t()))
+    with pytest.raises(ValueError):
+        vit.vit_merge2x2_layernorm(x, [(2, 2)], g.repeat(4), g.repeat(4), out=torch.empty((1, 512), dtype=torch.bfloat16))

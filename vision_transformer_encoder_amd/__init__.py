@@ -147,6 +147,16 @@ def _host_i32(a) -> Tuple[np.ndarray, int]:
     return arr, arr.ctypes.data
 
 
+def _out_like(given: Optional[torch.Tensor], shape, dtype, dev) -> torch.Tensor:
+    """A caller-provided output buffer (checked: contiguous, shape, dtype) or
+    a new one."""
+    if given is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if tuple(given.shape) != tuple(shape) or given.dtype != dtype or not given.is_contiguous():
+        raise ValueError(f"output buffer must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return given
+
+
 def _row_ld(t: torch.Tensor) -> int:
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError("2-D tensor with unit column stride expected")
@@ -168,15 +178,17 @@ def vit_status_string(status: int) -> str:
     return require_library().vit_status_string(status).decode()
 
 
-def vit_quant_fp8_block128(x: torch.Tensor, cols: Optional[int] = None, block_rows: int = 1):
+def vit_quant_fp8_block128(x: torch.Tensor, cols: Optional[int] = None, block_rows: int = 1,
+                           out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
     """Block-128 FP8 quantisation of a bf16 [rows, >=cols] tensor.
     Returns (codes uint8 [Rp, Cp], scales float32)."""
     rows = x.shape[0]
     cols = x.shape[1] if cols is None else cols
     cp = (cols + 127) // 128 * 128
     rp = rows if block_rows == 1 else (rows + 127) // 128 * 128
-    codes = torch.empty((rp, cp), dtype=torch.uint8, device=x.device)
-    scales = torch.empty(((rows + block_rows - 1) // block_rows, cp // 128), dtype=torch.float32, device=x.device)
+    oc, os_ = out if out is not None else (None, None)
+    codes = _out_like(oc, (rp, cp), torch.uint8, x.device)
+    scales = _out_like(os_, ((rows + block_rows - 1) // block_rows, cp // 128), torch.float32, x.device)
     _call("vit_quant_fp8_block128", _p(x), _row_ld(x), rows, cols, block_rows, _p(codes), _p(scales),
           _stream(x.device))
     return codes, scales
@@ -190,10 +202,11 @@ def vit_e4m3_encode(x: torch.Tensor) -> torch.Tensor:
 
 
 def vit_layernorm_quant_fp8(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float = 1e-6,
-                            prequant: bool = False):
+                            prequant: bool = False, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
     M, D = x.shape
-    codes = torch.empty((M, D), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((M, D // 128), dtype=torch.float32, device=x.device)
+    oc, os_ = out if out is not None else (None, None)
+    codes = _out_like(oc, (M, D), torch.uint8, x.device)
+    scales = _out_like(os_, (M, D // 128), torch.float32, x.device)
     pre = torch.empty((M, D), dtype=torch.float32, device=x.device) if prequant else None
     _call("vit_layernorm_quant_fp8", _p(x), _row_ld(x), _p(gamma), _p(beta), eps, M, D, _p(codes), _p(scales),
           _p(pre), _stream(x.device))
@@ -203,17 +216,19 @@ def vit_layernorm_quant_fp8(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Te
 def vit_fp8_block128_gemm(a: torch.Tensor, a_scales: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor,
                           N: int, K: int, bias: Optional[torch.Tensor] = None,
                           residual: Optional[torch.Tensor] = None, epilogue: int = EPI_BIAS,
-                          out: Optional[torch.Tensor] = None, prequant: bool = False):
+                          out=None, prequant: bool = False):
     """Block-scaled FP8 GEMM.  EPI_BIAS / EPI_BIAS_RESIDUAL return the bf16
     [M, N] output (``out`` may be given, and may be ``residual`` for an
-    in-place add); EPI_BIAS_GELU_FP8 returns (codes, scales[, prequant])."""
+    in-place add); EPI_BIAS_GELU_FP8 returns (codes, scales[, prequant])
+    (``out`` may be given as the (codes, scales) pair)."""
     M = a.shape[0]
     np_ = (N + 127) // 128 * 128
     dev = a.device
     codes = scales = pre = None
     if epilogue == EPI_BIAS_GELU_FP8:
-        codes = torch.empty((M, np_), dtype=torch.uint8, device=dev)
-        scales = torch.empty((M, np_ // 128), dtype=torch.float32, device=dev)
+        oc, os_ = out if out is not None else (None, None)
+        codes = _out_like(oc, (M, np_), torch.uint8, dev)
+        scales = _out_like(os_, (M, np_ // 128), torch.float32, dev)
         pre = torch.empty((M, np_), dtype=torch.float32, device=dev) if prequant else None
     elif out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -277,12 +292,12 @@ def vit_attention_workspace_size() -> int:
 
 def vit_merge2x2_layernorm(x: torch.Tensor, grids: Sequence[Tuple[int, int]], gamma: torch.Tensor,
                            beta: torch.Tensor, eps: float = 1e-6,
-                           grid_dev: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           grid_dev: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     T, D = x.shape
     g_h, g_ptr = _host_i32(np.asarray(grids, dtype=np.int32).reshape(-1, 2))
     if grid_dev is None:
         grid_dev = torch.from_numpy(g_h.copy()).to(x.device)
-    out = torch.empty((T // 4, 4 * D), dtype=torch.bfloat16, device=x.device)
+    out = _out_like(out, (T // 4, 4 * D), torch.bfloat16, x.device)
     _call("vit_merge2x2_layernorm", _p(x), D, _p(grid_dev), g_ptr, len(g_h), T, _p(gamma), _p(beta), eps,
           _p(out), _stream(x.device))
     return out

@@ -36,7 +36,10 @@ FLAGS = [
 # Per-source additions.  attention.hip: every value its max reductions see is
 # finite (masked keys carry a large finite negative score), so the NaN
 # quieting that IEEE fmaxf otherwise needs before each v_max is dropped.
-EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+# gemm.hip: MFMA results stay in VGPRs; left to its heuristics the compiler
+# parks the per-K-block partial sums in AGPRs, and every promotion FMA then
+# needs a v_accvgpr_read first.
+EXTRA = {"attention.hip": ["-fno-honor-nans"], "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 MAX_SCRATCH = 32  # bytes per lane
 
 

@@ -30,9 +30,13 @@
 //  * Software pipeline across key tiles: while the VALU turns S(j) into P(j)
 //    (exp2 with the scale folded in), the MFMA unit already computes S(j+1);
 //    then the PV MFMAs of tile j run, interleaved by hand with the row max
-//    of S(j+1).  K and V^T tiles live in a 3-buffer LDS ring (tile j: V^T
-//    read, tile j+1: K read, tile j+2: being written), one barrier per tile;
-//    global loads of tile j+3 are in flight during tile j.
+//    of S(j+1).  K and V^T tiles live in a 4-buffer LDS ring with one
+//    barrier per tile; a tile is stored two steps before its K is read, and
+//    its global loads are issued two steps before that (two register sets).
+//  * The two waves that share a SIMD run opposite phases: waves 4..7 take
+//    each tile's barrier between their QK/exp phase (VALU-heavy) and their
+//    PV phase (MFMA-heavy), waves 0..3 after the PV phase, so one wave's
+//    exp work overlaps the other's PV MFMAs.
 //  * The running max is only raised (and O rescaled) when a row max grows
 //    by more than 2^8 over it: exact after the final division by the row
 //    sum, and it removes the per-tile rescale of 48 accumulators.
@@ -43,9 +47,10 @@
 //    fixed for the whole loop (no per-tile address arithmetic), and rows
 //    past the last token read as zero in hardware, so no clamping is needed
 //    (rows of the next window inside the batch are finite and masked).
-//  * Items are ordered head-major and workgroup ids are mapped so that each
-//    XCD takes a contiguous run of ranges: an XCD's workgroups share one or
-//    two heads' K/V in its own L2.
+//  * Items are ordered head-major and cut into 2 x (workgroups) ranges;
+//    workgroup g runs ranges g and g + G, and ids are mapped so that each
+//    XCD takes a contiguous run: an XCD's 32 workgroups work on one head at
+//    a time, whose K/V then stays in the XCD's L2 (two heads do not fit).
 #include <algorithm>
 #include <atomic>
 
@@ -65,7 +70,22 @@ constexpr int kVS = 68;           // V^T row stride in LDS (bf16): 64 used
 constexpr int kKBuf = kBK * kKS;  // elements per K buffer
 constexpr int kVRows = kHD + 2;  // V^T rows 0..71, row 72 = ones, row 73 = zeros
 constexpr int kVBuf = kVRows * kVS;
-constexpr int kStages = 3;
+#ifndef VIT_ATTN_SKEW
+#define VIT_ATTN_SKEW 1
+#endif
+// Wave groups: the "late" group (one wave of each SIMD) takes the barrier of
+// a key tile between its QK/exp phase and its PV phase, the other group after
+// the PV phase.  The two waves that share a SIMD thus run opposite phases (one
+// VALU-heavy, one MFMA-heavy) instead of competing for the same unit.
+// 0: no late group; 1: waves 4..7; 2: odd waves.
+constexpr int kSkew = VIT_ATTN_SKEW;
+// A tile is stored kAhead steps before the step whose QK phase reads it, and
+// its stage is reused kStages tiles later.  Between a barrier and the next,
+// the early group runs QK(j) PV(j) and the late group PV(j-1) QK(j): the late
+// group's reads of V(j) fall one barrier interval after the early group's,
+// which the fourth stage covers.
+constexpr int kAhead = 2;
+constexpr int kStages = 4;
 constexpr float kLazy = 8.0f;     // rescale only when the max grows by > 2^8
 #ifndef VIT_ATTN_FRAG_AHEAD
 #define VIT_ATTN_FRAG_AHEAD 2
@@ -76,6 +96,10 @@ constexpr int kFragAhead = VIT_ATTN_FRAG_AHEAD;  // LDS operand fragments read t
 __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
+
+// Workgroup barrier for the LDS ring: this wave's LDS writes are complete,
+// its global loads in flight are not waited for (they only feed registers).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Staging of one K/V tile.  K: 64 rows x 9 chunks of 16 B = 576 chunks,
 // thread t owns chunks t, t + kThreads, ... (below 576).  V: 16 groups of 4 keys
@@ -253,10 +277,11 @@ __device__ __forceinline__ float tile_max(const f32x16_t s[2], float scale_log2)
 // Consecutive MFMAs write different accumulators, LDS operand fragments are
 // read two MFMAs ahead, and sched_barrier keeps the compiler from regrouping
 // the slots.  Returns the scaled row max of S(j+1).
+template <class Stage>
 __device__ __forceinline__ float tile_step(f32x16_t s_nxt[2], f32x16_t acc[3], const f32x16_t s_cur[2],
                                            const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vt,
                                            const bf16x8_t qf[5], float scale_log2, float m, int l32, int g,
-                                           int vrow2) {
+                                           int vrow2, Stage&& stage) {
   // K fragment i: key half jt = i & 1, d chunk kc = i >> 1
   const uint16_t* kr = ks + l32 * kKS + 8 * g;
   auto k_frag = [&](int i) { return ld_bf16x8(kr + (i & 1) * 32 * kKS + 16 * (i >> 1)); };
@@ -279,6 +304,7 @@ __device__ __forceinline__ float tile_step(f32x16_t s_nxt[2], f32x16_t acc[3], c
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[jc][rr + 1], scale_log2, -m));
       pw[e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
     }
+    stage(i);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -301,6 +327,7 @@ __device__ __forceinline__ float tile_step(f32x16_t s_nxt[2], f32x16_t acc[3], c
     // keep this slot's share of the max here (IR passes would otherwise
     // sink the whole reduction past the last MFMA)
     asm volatile("" : "+v"(ma), "+v"(mb));
+    stage(10 + i);
     __builtin_amdgcn_sched_barrier(0);
   }
   return halves_max(fmaxf(ma, mb)) * scale_log2;
@@ -318,6 +345,15 @@ constexpr uint32_t kMaskedKey = 0xff7fu;  // bf16 -3.39e38
 constexpr int kSlotRows = kHD + 2;
 constexpr int kSlotFloats = kSlotRows * kBQ;
 constexpr int kMaxWorkgroups = 256;
+// The work order is cut into rounds x workgroups equal ranges; workgroup g
+// runs ranges g, g + G, ... in turn.  With the XCD-grouped workgroup ids, the
+// workgroups of one XCD then share one head at a time (with 16 heads and 8
+// XCDs, two rounds): one head's K/V fits in the XCD's L2, where two do not.
+constexpr int kMaxRounds = 2;
+constexpr int kMaxRanges = kMaxWorkgroups * kMaxRounds;
+#ifndef VIT_ATTN_ROUNDS
+#define VIT_ATTN_ROUNDS 0
+#endif
 
 struct AttnParams {
   const uint16_t* q;
@@ -325,11 +361,11 @@ struct AttnParams {
   const uint16_t* v;
   uint16_t* o;
   const int32_t* cu;
-  float* partial;         // [2 * num_wgs][kSlotRows][kBQ]
+  float* partial;         // [2 * num_ranges][kSlotRows][kBQ]
   int64_t ld, ldo;
   int64_t work_per_head;  // sum over windows of (q tiles x key tiles)
   int64_t work;           // work_per_head * heads
-  int num_seqs, heads, total, num_wgs;
+  int num_seqs, heads, total, num_wgs, num_ranges;
   float scale_log2;
 };
 
@@ -340,7 +376,9 @@ struct Segment {
   int head, seq_begin, seq_len, qtile, kt, nk;  // kt: first key tile of the segment
 };
 
-__device__ __forceinline__ int64_t wg_start(const AttnParams& a, int g) { return (int64_t)g * a.work / a.num_wgs; }
+__device__ __forceinline__ int64_t range_start(const AttnParams& a, int r) {
+  return (int64_t)r * a.work / a.num_ranges;
+}
 
 // Item and key tile at position p of the work order (p < work).
 __device__ Segment locate(const AttnParams& a, int64_t p) {
@@ -367,6 +405,7 @@ __device__ Segment locate(const AttnParams& a, int64_t p) {
 // Key tiles [s.kt, kt_end) of one item: the pipelined flash loop.  With
 // slot == nullptr the segment covers the whole key range and writes the
 // normalised bf16 output, otherwise its partial (O, l, m) goes to slot.
+template <bool kLate>
 __device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& s, int kt_end, float* slot,
                                             uint16_t* __restrict__ ks_mem, uint16_t* __restrict__ vt_mem) {
   // an opaque copy of the thread id: addresses derived from it are rebuilt
@@ -418,20 +457,24 @@ __device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& 
   for (int dt = 0; dt < 3; ++dt) acc[dt] = f32x16_t{};
   float m_run = -INFINITY;  // running max of scaled scores (log2 units)
 
-  // ---- prologue: the segment's tiles 0 and 1 into stages 0 and 1, tile 2
-  // into registers (loads past the window are harmless: see load_kv)
+  // ---- prologue: the segment's tiles 0 .. kAhead-1 into stages 0 .. kAhead-1,
+  // tile kAhead into registers (loads past the window are harmless: see load_kv)
   const KVPlan plan = make_plan(tid, ld, hoff);
-  KVRegs r;
   {
-    KVRegs r1;
-    load_kv(r, plan, a.k, a.v, ld, row0, a.total, tid);
-    load_kv(r1, plan, a.k, a.v, ld, row0 + kBK, a.total, tid);
-    store_kv(r, plan, ks_mem, vt_mem, tid);
-    mask_last(s.kt, 0);
-    store_kv(r1, plan, ks_mem + kKBuf, vt_mem + kVBuf, tid);
-    mask_last(s.kt + 1, 1);
+    KVRegs pre[kAhead];
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) load_kv(pre[t], plan, a.k, a.v, ld, row0 + t * kBK, a.total, tid);
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) {
+      store_kv(pre[t], plan, ks_mem + t * kKBuf, vt_mem + t * kVBuf, tid);
+      mask_last(s.kt + t, t);
+    }
   }
-  load_kv(r, plan, a.k, a.v, ld, row0 + 2 * kBK, a.total, tid);
+  // two register sets: a tile's global load is issued two tile steps before
+  // its LDS store
+  KVRegs r_a, r_b;
+  load_kv(r_a, plan, a.k, a.v, ld, row0 + kAhead * kBK, a.total, tid);
+  load_kv(r_b, plan, a.k, a.v, ld, row0 + (kAhead + 1) * kBK, a.total, tid);
   __syncthreads();
 
   f32x16_t s_a[2], s_b[2];
@@ -449,19 +492,24 @@ __device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& 
   };
 
   int bv = 0;  // stage holding tile j
-  // Tile j (j < ntiles - 1).  Tile j+2 goes from registers to LDS and tile
-  // j+3 is fetched (past the segment these are harmless extra loads into a
-  // free stage).  Then the interleaved MFMA/VALU work of the tile.
-  auto body = [&](int j, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2]) {
-    const int bk = bv == kStages - 1 ? 0 : bv + 1;  // stage of tile j+1
-    const int bw = bk == kStages - 1 ? 0 : bk + 1;  // stage for tile j+2
+  auto next_stage = [](int st, int n) { return st + n >= kStages ? st + n - kStages : st + n; };
+  // Tile j (j < ntiles - 1).  Tile j+kAhead goes from registers r to LDS and
+  // tile j+kAhead+2 is fetched into r (past the segment these are harmless
+  // extra loads into a free stage).  Then the interleaved MFMA/VALU work of
+  // the tile, with this wave group's barrier after its QK or its PV phase.
+  auto body = [&](int j, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2], KVRegs& r) {
+    const int bk = next_stage(bv, 1);       // stage of tile j+1
+    const int bw = next_stage(bv, kAhead);  // stage for tile j+kAhead
     rescale();
     store_kv(r, plan, ks_mem + bw * kKBuf, vt_mem + bw * kVBuf, tid);
-    mask_last(s.kt + j + 2, bw);
-    load_kv(r, plan, a.k, a.v, ld, row0 + (j + 3) * kBK, a.total, tid);
+    mask_last(s.kt + j + kAhead, bw);
+    load_kv(r, plan, a.k, a.v, ld, row0 + (j + kAhead + 2) * kBK, a.total, tid);
+    auto hook = [&](int slot) {
+      if (kLate && slot == 9) lds_barrier();
+    };
     mx = tile_step(s_nxt, acc, s_cur, ks_mem + bk * kKBuf, vt_mem + bv * kVBuf, qf, scale_log2, m_run, l32, g,
-                   vrow2);
-    __syncthreads();
+                   vrow2, hook);
+    if (!kLate) lds_barrier();
     bv = bk;
   };
   // Last tile: P and PV only.
@@ -472,14 +520,15 @@ __device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& 
     pv_tile(acc, vt_mem + bv * kVBuf, pb, l32, g, vrow2);
   };
 
-  // two tiles per trip with the S registers swapping roles: no copies
+  // two tiles per trip with the S registers and the staging register sets
+  // swapping roles: no copies
   int j = 0;
   for (; j + 2 < ntiles; j += 2) {
-    body(j, s_a, s_b);
-    body(j + 1, s_b, s_a);
+    body(j, s_a, s_b, r_a);
+    body(j + 1, s_b, s_a, r_b);
   }
   if (j + 1 < ntiles) {
-    body(j, s_a, s_b);
+    body(j, s_a, s_b, r_a);
     tail(s_b);
   } else {
     tail(s_a);
@@ -536,36 +585,44 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams a) {
     *reinterpret_cast<uint32_t*>(vt_mem + st * kVBuf + row * kVS + col) = row == 72 ? 0x3f803f80u : 0u;
   }
 
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool late = kSkew == 1 ? wave >= 4 : kSkew == 2 ? (wave & 1) != 0 : false;
   const int lg = xcd_logical_block(blockIdx.x, a.num_wgs);
-  int64_t p = wg_start(a, lg);
-  const int64_t end = wg_start(a, lg + 1);
-  while (p < end) {
-    const Segment s = locate(a, p);
-    if (s.nk == 0) break;  // only if the device windows disagree with the host's work count
-    const int kt_end = (int)min((int64_t)s.nk, s.kt + (end - p));
-    // a segment that starts inside its item uses slot 2g, one that starts
-    // the item but stops short of its end slot 2g + 1
-    float* slot = (s.kt == 0 && kt_end == s.nk) ? nullptr
-                                                : a.partial + (size_t)(2 * lg + (s.kt != 0 ? 0 : 1)) * kSlotFloats;
-    run_segment(a, s, kt_end, slot, ks_mem, vt_mem);
-    p += kt_end - s.kt;
+  for (int rg = lg; rg < a.num_ranges; rg += a.num_wgs) {
+    int64_t p = range_start(a, rg);
+    const int64_t end = range_start(a, rg + 1);
+    while (p < end) {
+      const Segment s = locate(a, p);
+      if (s.nk == 0) break;  // only if the device windows disagree with the host's work count
+      const int kt_end = (int)min((int64_t)s.nk, s.kt + (end - p));
+      // a segment that starts inside its item uses slot 2 rg, one that starts
+      // the item but stops short of its end slot 2 rg + 1
+      float* slot = (s.kt == 0 && kt_end == s.nk)
+                        ? nullptr
+                        : a.partial + (size_t)(2 * rg + (s.kt != 0 ? 0 : 1)) * kSlotFloats;
+      if (late)
+        run_segment<true>(a, s, kt_end, slot, ks_mem, vt_mem);
+      else
+        run_segment<false>(a, s, kt_end, slot, ks_mem, vt_mem);
+      p += kt_end - s.kt;
+    }
   }
 }
 
 // Merge the partials of every item that the stream-K ranges cut.  The
-// workgroup whose range holds an item's last key tile does it, reading the
+// block of the range that holds an item's last key tile does it, reading the
 // item's segments in key order (deterministic):
 //   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  O = sum_s 2^(m_s - m) O_s / l.
 __global__ __launch_bounds__(2 * kBQ) void attention_combine_kernel(AttnParams a) {
-  const int lg = blockIdx.x;
-  const int64_t p = wg_start(a, lg), end = wg_start(a, lg + 1);
+  const int lg = blockIdx.x;  // range
+  const int64_t p = range_start(a, lg), end = range_start(a, lg + 1);
   if (p >= end) return;
   const Segment s = locate(a, p);
   if (s.nk == 0 || s.kt == 0 || s.kt + (end - p) < s.nk) return;  // not an item's last segment
   const int64_t p0 = p - s.kt;                        // the item's first key tile
-  int g0 = (int)(p0 * a.num_wgs / a.work);
-  while (g0 + 1 < a.num_wgs && wg_start(a, g0 + 1) <= p0) ++g0;
-  while (g0 > 0 && wg_start(a, g0) > p0) --g0;
+  int g0 = (int)(p0 * a.num_ranges / a.work);
+  while (g0 + 1 < a.num_ranges && range_start(a, g0 + 1) <= p0) ++g0;
+  while (g0 > 0 && range_start(a, g0) > p0) --g0;
 
   const int tid = threadIdx.x, qi = tid & (kBQ - 1), half = tid / kBQ;
   const int q_local = s.qtile * kBQ + qi;
@@ -607,7 +664,7 @@ int64_t attention_work_per_head(const int32_t* cu_host, int num_seqs) {
   return n;
 }
 
-size_t attention_partial_bytes() { return (size_t)2 * kMaxWorkgroups * kSlotFloats * sizeof(float); }
+size_t attention_partial_bytes() { return (size_t)2 * kMaxRanges * kSlotFloats * sizeof(float); }
 
 // Resident slots of the current device: one 512-thread workgroup per CU,
 // at most kMaxWorkgroups.
@@ -644,13 +701,16 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   a.num_seqs = num_seqs;
   a.heads = heads;
   a.total = total_tokens;
-  // every workgroup must own at least one key tile
+  // every range must own at least one key tile; one round per 8 heads (the
+  // XCD count), at most kMaxRounds
+  const int rounds = std::min(kMaxRounds, VIT_ATTN_ROUNDS > 0 ? VIT_ATTN_ROUNDS : std::max(1, heads / 8));
   a.num_wgs = (int)std::min<int64_t>(attention_slots(), a.work);
+  a.num_ranges = (int)std::min<int64_t>((int64_t)a.num_wgs * rounds, a.work);
   a.scale_log2 = scale * 1.4426950408889634f;
   attention_kernel<<<a.num_wgs, kThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  attention_combine_kernel<<<a.num_wgs, 2 * kBQ, 0, stream>>>(a);
+  attention_combine_kernel<<<a.num_ranges, 2 * kBQ, 0, stream>>>(a);
   return hipGetLastError();
 }
 
