@@ -1,0 +1,43 @@
+"""The whole tower captured as one HIP graph (torch.cuda.CUDAGraph around
+vit_encoder_forward, which allocates nothing and never synchronises) and
+replayed: every replay must equal the eager forward bit for bit, with eager
+work and synchronisations of the program between the replays."""
+
+import pytest
+import torch
+
+import synth
+import vision_transformer_encoder_amd as vit
+from gpu_util import announce
+
+pytestmark = pytest.mark.gpu
+
+
+def test_encoder_graph_replays_match_eager(gpu):
+    ep = synth.encoder_params(0)
+    W = vit.EncoderWeights(ep.patch, ep.blocks, ep.mergers, gpu)
+    grids = [(18, 54), (12, 20)]  # two windows, 972 + 240 tokens
+    T = sum(h * w for h, w in grids)
+    px = torch.from_numpy(synth.pixels(1, T)).to(gpu)
+    px_other = torch.from_numpy(synth.pixels(2, T)).to(gpu)
+    grid_dev = torch.tensor(grids, dtype=torch.int32, device=gpu)
+    ws = torch.empty(vit.vit_encoder_workspace_size(T, len(grids)), dtype=torch.uint8, device=gpu)
+    out = torch.empty((4, T // 4, 4096), dtype=torch.bfloat16, device=gpu)
+    announce(f"vit_encoder_forward eager reference T={T}")
+    ref, _ = vit.vit_encoder_forward(W, px, grids, grid_dev=grid_dev)
+    torch.cuda.synchronize()
+
+    announce("capture")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        vit.vit_encoder_forward(W, px, grids, workspace=ws, out=out, grid_dev=grid_dev)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        # eager work on the same buffers between the replays
+        out.fill_(0)
+        vit.vit_encoder_forward(W, px_other, grids, workspace=ws, out=out, grid_dev=grid_dev)
+        torch.cuda.synchronize()
+        announce(f"replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep} differs from eager"
