@@ -387,13 +387,22 @@ class BlockWeights:
 @dataclass
 class MergerWeights:
     """One 2x2 merger MLP (spark_model page, struct MergerLayer: norm w/b,
-    fc1 w/b, fc2 w/b), bf16 (FlashRT section 4: mergers stay bf16)."""
+    fc1 w/b, fc2 w/b), bf16 (FlashRT section 4: mergers stay bf16); the FP8
+    variant ("merger FP8", FlashRT section 1 prefill history) uses
+    quantize_block128(., 128) of the same bf16 weights."""
     ln_g: np.ndarray    # [4608]
     ln_b: np.ndarray
     fc1_w: np.ndarray   # [4608, 4608]
     fc1_b: np.ndarray
     fc2_w: np.ndarray   # [4096, 4608]
     fc2_b: np.ndarray
+    _q: Dict[str, Fp8Weight] = field(default_factory=dict, repr=False)
+
+    def fp8(self, name: str) -> Fp8Weight:
+        if name not in self._q:
+            codes, scales = quantize_block128(getattr(self, name + "_w"), BLOCK)
+            self._q[name] = Fp8Weight(codes, scales)
+        return self._q[name]
 
 
 @dataclass
@@ -455,6 +464,31 @@ def _rb(x, storage):
     return bf16(x) if storage else np.asarray(x, dtype=np.float64)
 
 
+def block_forward_bf16(x, w: BlockWeights, pos_rc, cu_seqlens, mode: str = "storage",
+                       trace: Optional[dict] = None) -> np.ndarray:
+    """One pre-norm ViT block with bf16 GEMMs and no FP8 anywhere: the
+    precision FlashRT section 4 keeps for the first 3 blocks ("patch embed,
+    the mergers and the first 3 blocks stay bf16").  Same chain as
+    block_forward; the LayerNorm outputs and the GELU output, which feed
+    GEMMs, are stored in bf16 (there is no quantiser to take fp32).
+    """
+    storage = mode == "storage"
+    x = np.asarray(x, dtype=np.float64)
+    y1 = _rb(layernorm(x, w.ln1_g, w.ln1_b), storage)
+    qkv = _rb(bf16_gemm(y1, w.qkv_w, w.qkv_b), storage)
+    q, k, v = qkv[:, :HIDDEN], qkv[:, HIDDEN:2 * HIDDEN], qkv[:, 2 * HIDDEN:]
+    q = _rb(rope2d(q, pos_rc), storage)
+    k = _rb(rope2d(k, pos_rc), storage)
+    o = _rb(attention(q, k, v, cu_seqlens), storage)
+    x1 = _rb(bf16_gemm(o, w.proj_w, w.proj_b) + x, storage)
+    y2 = _rb(layernorm(x1, w.ln2_g, w.ln2_b), storage)
+    h = _rb(gelu_tanh(bf16_gemm(y2, w.fc1_w, w.fc1_b)), storage)
+    x2 = _rb(bf16_gemm(h, w.fc2_w, w.fc2_b) + x1, storage)
+    if trace is not None:
+        trace.update(dict(y1=y1, qkv=qkv, q=q, k=k, o=o, x1=x1, y2=y2, h=h, x2=x2))
+    return x2
+
+
 def block_forward(x, w: BlockWeights, pos_rc, cu_seqlens, mode: str = "storage",
                   trace: Optional[dict] = None) -> np.ndarray:
     """One pre-norm ViT block (FlashRT section 3 "per block: LayerNorm -> qkv
@@ -501,16 +535,28 @@ def block_forward(x, w: BlockWeights, pos_rc, cu_seqlens, mode: str = "storage",
     return x2
 
 
-def merger_forward(x, m: MergerWeights, grids, mode: str = "storage") -> np.ndarray:
+def merger_forward(x, m: MergerWeights, grids, mode: str = "storage", fp8: bool = False) -> np.ndarray:
     """2x2 merge -> LayerNorm(4608) -> fc1 (+b) -> GELU(tanh) -> fc2 (+b),
     bf16 (FlashRT section 3 "2x2 patch merger -> image_embeds (out_hidden
     4096)"; spark_model page struct MergerLayer).  Readings: LayerNorm over
-    the concatenated 4608 features for all four mergers, tanh-GELU."""
+    the concatenated 4608 features for all four mergers, tanh-GELU.
+
+    fp8=True is the "merger FP8" of FlashRT section 1 with the blocks' W8A8
+    recipe: the bf16 LayerNorm output is quantised per token and 128
+    columns, fc1 + bias + GELU is requantised the same way (from fp32),
+    fc2 + bias is stored in bf16; weights quantised in 128 x 128 blocks."""
     storage = mode == "storage"
     y = merge2x2(x, grids)
     y = _rb(layernorm(y, m.ln_g, m.ln_b), storage)
-    h = _rb(gelu_tanh(bf16_gemm(y, m.fc1_w, m.fc1_b)), storage)
-    return _rb(bf16_gemm(h, m.fc2_w, m.fc2_b), storage)
+    if not fp8:
+        h = _rb(gelu_tanh(bf16_gemm(y, m.fc1_w, m.fc1_b)), storage)
+        return _rb(bf16_gemm(h, m.fc2_w, m.fc2_b), storage)
+    a, sa = quantize_block128(y, 1)
+    f1, f2 = m.fp8("fc1"), m.fp8("fc2")
+    hc, hs, _ = fp8_gemm_epilogue(fp8_block128_gemm(a, sa, f1.codes, f1.scales), MERGED_DIM,
+                                  EPI_BIAS_GELU_FP8, bias=m.fc1_b)
+    return fp8_gemm_epilogue(fp8_block128_gemm(hc, hs, f2.codes, f2.scales), OUT_HIDDEN, EPI_BIAS,
+                             bias=m.fc2_b, storage=storage)
 
 
 def patch_embed(pixels, w: EncoderWeights, pos_embed=None, mode: str = "storage") -> np.ndarray:
@@ -525,10 +571,13 @@ def patch_embed(pixels, w: EncoderWeights, pos_embed=None, mode: str = "storage"
 
 def encoder_forward(pixels, w: EncoderWeights, grids, pos_embed=None,
                     mode: str = "storage", depth: int = DEPTH,
-                    taps: Sequence[int] = TAPS, trace: Optional[dict] = None):
+                    taps: Sequence[int] = TAPS, trace: Optional[dict] = None,
+                    bf16_blocks: int = 0, fp8_mergers: bool = False):
     """Whole vision tower (FlashRT section 3): patch embed, blocks 1..27, the
     DeepStack taps after blocks 8/16/24 and the final block, each fed to its
-    2x2 merger MLP.  Returns (out [len(taps), T/4, 4096], last hidden)."""
+    2x2 merger MLP.  Returns (out [len(taps), T/4, 4096], last hidden).
+    Precision variants (FlashRT section 4 and section 1): the first
+    ``bf16_blocks`` blocks with bf16 GEMMs, FP8 mergers."""
     cu = cu_seqlens_from_grids(grids)
     pos = positions_from_grids(grids)
     x = patch_embed(pixels, w, pos_embed, mode)
@@ -537,11 +586,12 @@ def encoder_forward(pixels, w: EncoderWeights, grids, pos_embed=None,
     if trace is not None:
         trace["x0"] = x
     for b in range(1, depth + 1):
-        x = block_forward(x, w.blocks[b - 1], pos, cu, mode)
+        fwd = block_forward_bf16 if b <= bf16_blocks else block_forward
+        x = fwd(x, w.blocks[b - 1], pos, cu, mode)
         if trace is not None:
             trace[f"x{b}"] = x
         if ti < len(taps) and b == taps[ti]:
-            outs.append(merger_forward(x, w.mergers[ti], grids, mode))
+            outs.append(merger_forward(x, w.mergers[ti], grids, mode, fp8=fp8_mergers))
             ti += 1
     return np.stack(outs, axis=0), x
 

@@ -103,6 +103,109 @@ def test_block_storage_vs_pure_close():
     assert tr["h_codes"].shape == (16, 4352) and np.all(tr["h_codes"][:, 4304:] == 0)
 
 
+# ---- precision variants: bf16 blocks (FlashRT section 4), FP8 mergers
+# (FlashRT section 1)
+
+def _cos_rel(a, b):
+    a, b = np.ravel(a), np.ravel(b)
+    return float(a @ b / np.linalg.norm(a) / np.linalg.norm(b)), float(np.abs(a - b).max() / np.abs(b).max())
+
+
+def test_bf16_block_with_zero_weights_is_identity():
+    p = OI.zero_like_block(_small_block(), keep=["ln1_g", "ln1_b", "ln2_g", "ln2_b"])
+    w = OI.block_weights(p)
+    grids = [(4, 4)]
+    x = _x(16)
+    y = O.block_forward_bf16(x, w, O.positions_from_grids(grids), O.cu_seqlens_from_grids(grids))
+    assert np.array_equal(y, x)
+
+
+def test_bf16_block_residual_wiring():
+    # proj and fc2 zero: both branches add exactly their bias
+    p = dict(_small_block())
+    for n in ("proj_w", "fc2_w"):
+        p[n] = np.zeros_like(p[n])
+    w = OI.block_weights(p)
+    grids = [(4, 4)]
+    x = _x(16)
+    y = O.block_forward_bf16(x, w, O.positions_from_grids(grids), O.cu_seqlens_from_grids(grids))
+    assert np.array_equal(y, O.bf16(O.bf16(x + w.proj_b) + w.fc2_b))
+
+
+def test_bf16_block_varlen_packed_equals_separate():
+    w = OI.block_weights(_small_block())
+    grids = [(2, 4), (4, 6)]
+    x = _x(32)
+    packed = O.block_forward_bf16(x, w, O.positions_from_grids(grids), O.cu_seqlens_from_grids(grids))
+    a = O.block_forward_bf16(x[:8], w, O.positions_from_grids(grids[:1]), [0, 8])
+    b = O.block_forward_bf16(x[8:], w, O.positions_from_grids(grids[1:]), [0, 24])
+    assert np.array_equal(packed, np.concatenate([a, b]))
+
+
+def test_bf16_block_agrees_with_fp8_block():
+    # The two precisions compute the same block: their updates x2 - x agree
+    # to within FP8 quantisation noise (a dropped or mis-signed term in
+    # either path would not).  Larger weights make the update visible.
+    p = dict(_small_block())
+    for n in ("qkv_w", "proj_w", "fc1_w", "fc2_w"):
+        p[n] = synth.normal_bf16(0, n, 99, p[n].shape, std=0.05)
+    w = OI.block_weights(p)
+    grids = [(4, 8)]
+    x = _x(32)
+    pos, cu = O.positions_from_grids(grids), O.cu_seqlens_from_grids(grids)
+    p16 = O.block_forward_bf16(x, w, pos, cu, "pure")
+    d16 = p16 - x
+    d8 = O.block_forward(x, w, pos, cu, "pure") - x
+    # E4M3 keeps 3 mantissa bits: four quantised GEMMs put about 10 % rms
+    # noise on the update
+    cos, _ = _cos_rel(d8, d16)
+    rms = float(np.linalg.norm(d8 - d16) / np.linalg.norm(d16))
+    assert cos > 0.99 and rms < 0.15, (cos, rms)
+    # the bf16 storage points move the block output by bf16 rounding only
+    s16 = O.block_forward_bf16(x, w, pos, cu, "storage")
+    assert np.abs(s16 - p16).max() / np.abs(p16).max() < 2e-2
+
+
+def test_fp8_merger_zero_weights_gives_bias():
+    m = OI.merger_weights(synth.merger_params(0, 0))
+    m.fc1_w = np.zeros_like(m.fc1_w)
+    m.fc2_w = np.zeros_like(m.fc2_w)
+    grids = [(2, 4)]
+    x = _x(8)
+    y = O.merger_forward(x, m, grids, fp8=True)
+    assert np.array_equal(y, np.broadcast_to(O.bf16(m.fc2_b), (2, 4096)))
+
+
+def test_fp8_merger_agrees_with_bf16_merger():
+    m = OI.merger_weights(synth.merger_params(0, 0))
+    grids = [(4, 4), (2, 6)]
+    x = _x(28)
+    y8 = O.merger_forward(x, m, grids, "pure", fp8=True)
+    y16 = O.merger_forward(x, m, grids, "pure")
+    # the bias dominates the synthetic merger output: compare without it
+    d8, d16 = y8 - m.fc2_b, y16 - m.fc2_b
+    cos, _ = _cos_rel(d8, d16)
+    rms = float(np.linalg.norm(d8 - d16) / np.linalg.norm(d16))
+    assert cos > 0.99 and rms < 0.15, (cos, rms)
+
+
+def test_encoder_precision_variants_route_blocks_and_mergers():
+    ep = synth.EncoderParams(patch=synth.patch_params(0),
+                             blocks=[synth.block_params(0, b) for b in range(4)],
+                             mergers=[synth.merger_params(0, m) for m in range(2)])
+    W = OI.encoder_weights(ep)
+    grids = [(2, 4)]
+    px = synth.pixels(0, 8).astype(np.float64)
+    pos, cu = O.positions_from_grids(grids), O.cu_seqlens_from_grids(grids)
+    tr = {}
+    out, last = O.encoder_forward(px, W, grids, depth=4, taps=(1, 4), trace=tr, bf16_blocks=2, fp8_mergers=True)
+    assert np.array_equal(tr["x1"], O.block_forward_bf16(tr["x0"], W.blocks[0], pos, cu))
+    assert np.array_equal(tr["x2"], O.block_forward_bf16(tr["x1"], W.blocks[1], pos, cu))
+    assert np.array_equal(tr["x3"], O.block_forward(tr["x2"], W.blocks[2], pos, cu))
+    assert np.array_equal(out[0], O.merger_forward(tr["x1"], W.mergers[0], grids, fp8=True))
+    assert np.array_equal(out[1], O.merger_forward(tr["x4"], W.mergers[1], grids, fp8=True))
+
+
 def test_encoder_taps_are_block_outputs():
     # Short tower (depth 4, taps after blocks 1 and 4) built from the same
     # functions; the taps must be the mergers of those blocks' outputs.
