@@ -130,6 +130,9 @@ def main() -> int:
     ap.add_argument("--workload", default="encoder_p6256", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel event timings")
+    ap.add_argument("--bf16-blocks", type=int, default=0,
+                    help="precision variant: the first N blocks run LayerNorm and GEMMs in bf16 (the pages keep 3)")
+    ap.add_argument("--fp8-mergers", action="store_true", help="precision variant: FP8 merger linears")
     ap.add_argument("--graph", action="store_true",
                     help="capture the whole forward once as a HIP graph and time its replays")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -166,7 +169,11 @@ def main() -> int:
         print(json.dumps({"kernel": args.kernel, "workload": args.workload, **k[args.kernel]}), flush=True)
         return 0
     ep = synth.encoder_params(cfg)
-    W = vit.EncoderWeights(ep.patch, ep.blocks, ep.mergers, dev)
+    W = vit.EncoderWeights(ep.patch, ep.blocks, ep.mergers, dev, bf16_blocks=args.bf16_blocks,
+                           fp8_mergers=args.fp8_mergers)
+    variant = args.bf16_blocks > 0 or args.fp8_mergers
+    if variant:
+        args.no_kernels = True  # the per-kernel timing replays the all-FP8 block sequence
     px = torch.from_numpy(synth.pixels(cfg, T)).to(dev)
     g_host = np.asarray(grids, dtype=np.int32).reshape(-1, 2)
     g_dev = torch.from_numpy(g_host.copy()).to(dev)
@@ -245,6 +252,7 @@ def main() -> int:
                        "images_per_s": round(1e3 * nimg / ms_per_step, 2)},
         "outputs_finite": ok,
         "launch": "hip_graph" if args.graph else "eager",
+        "precision": {"bf16_blocks": args.bf16_blocks, "fp8_mergers": bool(args.fp8_mergers)},
     }
     if roofline is not None:
         line["roofline"] = roofline

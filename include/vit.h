@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define VIT_ABI_VERSION 2
+#define VIT_ABI_VERSION 3
 
 /* Model dimensions (FlashRT section 3; spark_model struct VisionEncoder). */
 #define VIT_HIDDEN 1152
@@ -116,6 +116,16 @@ int vit_layernorm_quant_fp8(const uint16_t* x, int64_t ld_x, const uint16_t* gam
                             const uint16_t* beta, float eps, int M, int D,
                             uint8_t* codes, float* scales, float* prequant_debug,
                             vit_stream_t stream);
+
+/* ---------------------------------------------------------------------
+ * LayerNorm with a bf16 result: the normalisation of the blocks that run
+ * their GEMMs in bf16 (FlashRT section 4: "the first 3 blocks stay bf16").
+ *   out = bf16((x - mean) / sqrt(var + eps) * gamma + beta)  (fp32 math)
+ * x: [M, ld_x] bf16; gamma, beta: [D] bf16; D % 128 == 0, D <= 8192;
+ * out: [M, ld_out] bf16, ld_out >= D.  out must not overlap x.
+ * ------------------------------------------------------------------- */
+int vit_layernorm(const uint16_t* x, int64_t ld_x, const uint16_t* gamma, const uint16_t* beta,
+                  float eps, int M, int D, uint16_t* out, int64_t ld_out, vit_stream_t stream);
 
 /* ---------------------------------------------------------------------
  * Block-scaled FP8 W8A8 GEMM with fused epilogues (FlashRT section 1:
@@ -229,6 +239,10 @@ int vit_merge2x2_layernorm(const uint16_t* x, int D, const int32_t* grid_hw_dev,
 /* ---------------------------------------------------------------------
  * Weights of one block (spark_model struct ViTBlock).  FP8 weights are
  * 128x128-block quantised with vit_quant_fp8_block128(block_rows = 128).
+ * Precision switch (FlashRT section 4: the first 3 blocks stay bf16): when
+ * qkv_w, proj_w, fc1_w and fc2_w are all set, the block runs LayerNorm and
+ * its four GEMMs in bf16 from them and the FP8 codes / scales may be NULL;
+ * when they are all NULL, it runs the FP8 recipe.  Mixed sets are rejected.
  * ------------------------------------------------------------------- */
 typedef struct vit_block_weights {
   const uint16_t* ln1_gamma;  /* [1152] bf16 */
@@ -247,9 +261,19 @@ typedef struct vit_block_weights {
   const uint8_t* fc2_codes;   /* [1152, 4352], columns >= 4304 zero */
   const float* fc2_scales;    /* [9, 34] */
   const uint16_t* fc2_bias;   /* [1152] */
+  const uint16_t* qkv_w;      /* [3456, 1152] bf16, or NULL */
+  const uint16_t* proj_w;     /* [1152, 1152] bf16, or NULL */
+  const uint16_t* fc1_w;      /* [4304, 1152] bf16, or NULL */
+  const uint16_t* fc2_w;      /* [1152, 4304] bf16, or NULL */
 } vit_block_weights;
 
-/* Weights of one 2x2 merger MLP (spark_model struct MergerLayer), bf16. */
+/* Weights of one 2x2 merger MLP (spark_model struct MergerLayer), bf16.
+ * Precision switch ("merger FP8", FlashRT section 1): when fc1_codes,
+ * fc1_scales, fc2_codes and fc2_scales are all set (128x128-block
+ * quantised like the block weights), the merger quantises its LayerNorm
+ * output per token and 128 columns and runs both linears as block-scaled
+ * FP8 GEMMs (GELU + requant fused into fc1); fc1_w / fc2_w may then be
+ * NULL.  When they are all NULL, it runs in bf16.  Mixed sets are rejected. */
 typedef struct vit_merger_weights {
   const uint16_t* ln_gamma;   /* [4608] */
   const uint16_t* ln_beta;    /* [4608] */
@@ -257,6 +281,10 @@ typedef struct vit_merger_weights {
   const uint16_t* fc1_b;      /* [4608] */
   const uint16_t* fc2_w;      /* [4096, 4608] */
   const uint16_t* fc2_b;      /* [4096] */
+  const uint8_t* fc1_codes;   /* [4608, 4608] E4M3, or NULL */
+  const float* fc1_scales;    /* [36, 36], or NULL */
+  const uint8_t* fc2_codes;   /* [4096, 4608] E4M3, or NULL */
+  const float* fc2_scales;    /* [32, 36], or NULL */
 } vit_merger_weights;
 
 typedef struct vit_encoder_weights {

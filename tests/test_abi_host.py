@@ -148,9 +148,17 @@ def test_merge_validation_statuses(lib):
     assert f(A, 1152, None, grids, 2, 28, C, D, 1e-6, E, None) == NULL
 
 
-def _block_struct(null_field=None, misalign=None):
+BF16_BLOCK_FIELDS = ("qkv_w", "proj_w", "fc1_w", "fc2_w")
+FP8_MERGER_FIELDS = ("fc1_codes", "fc1_scales", "fc2_codes", "fc2_scales")
+
+
+def _block_struct(null_field=None, misalign=None, bf16=False):
+    """An FP8 block (bf16 weight pointers NULL), or with bf16=True a block
+    whose bf16 weights are set as well."""
     s = vit._BlockW()
     for i, (name, _) in enumerate(vit._BlockW._fields_):
+        if name in BF16_BLOCK_FIELDS and not bf16:
+            continue
         setattr(s, name, A + i * (1 << 24))
     if null_field:
         setattr(s, null_field, None)
@@ -173,6 +181,30 @@ def test_block_validation(lib):
     assert f(ctypes.byref(s), X, 256, POS, CU, cu, 1, WSP + 64, need, None) == ALIGN   # 256-B workspace
     assert f(ctypes.byref(s), X, 256, POS, CU, cu, 1, X, need, None) == ALIAS          # x inside workspace
     assert f(None, X, 256, POS, CU, cu, 1, WSP, need, None) == NULL
+    # precision switch: a partial bf16 set is rejected, a complete one needs no FP8 codes
+    part = _block_struct()
+    part.qkv_w = A
+    assert f(ctypes.byref(part), X, 256, POS, CU, cu, 1, WSP, need, None) == NULL
+    assert f(ctypes.byref(_block_struct(bf16=True, misalign="fc2_w")), X, 256, POS, CU, cu, 1, WSP, need,
+             None) == ALIGN
+    assert f(ctypes.byref(_block_struct(bf16=True, null_field="qkv_codes")), X, 256, POS, CU, cu, 1, WSP,
+             need - 1, None) == WS
+
+
+def test_layernorm_validation(lib):
+    f = lib.vit_layernorm
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    X, G, Bt, O = A, B, B + 8192, C
+    assert f(X, 1152, G, Bt, 1e-6, 16, 1000, O, 1152, None) == SHAPE  # D % 128
+    assert f(X, 1000, G, Bt, 1e-6, 16, 1152, O, 1152, None) == SHAPE  # ld_x < D
+    assert f(X, 1152, G, Bt, 1e-6, 16, 1152, O, 1000, None) == SHAPE  # ld_out < D
+    assert f(X, 1152, G, Bt, -1.0, 16, 1152, O, 1152, None) == SHAPE  # eps
+    assert f(X, 1152, G, Bt, 1e-6, 0, 1152, O, 1152, None) == OK
+    assert f(None, 1152, G, Bt, 1e-6, 16, 1152, O, 1152, None) == NULL
+    assert f(X, 1156, G, Bt, 1e-6, 16, 1152, O, 1152, None) == ALIGN  # ld_x % 8
+    assert f(X + 8, 1152, G, Bt, 1e-6, 16, 1152, O, 1152, None) == ALIGN
+    assert f(X, 1152, G, Bt, 1e-6, 16, 1152, X + 1024, 1152, None) == ALIAS
 
 
 def test_encoder_validation(lib):
@@ -184,7 +216,8 @@ def test_encoder_validation(lib):
     for m in range(4):
         ms = vit._MergerW()
         for i, (name, _) in enumerate(vit._MergerW._fields_):
-            setattr(ms, name, B + i * (1 << 24))
+            if name not in FP8_MERGER_FIELDS:
+                setattr(ms, name, B + i * (1 << 24))
         w.mergers[m] = ms
     grids = _cu([46, 136])
     T = 6256
@@ -196,6 +229,9 @@ def test_encoder_validation(lib):
     w.mergers[2].fc2_w = None
     assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need, None) == NULL
     w.mergers[2].fc2_w = B
+    w.mergers[1].fc1_codes = B  # partial FP8 merger set
+    assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need, None) == NULL
+    w.mergers[1].fc1_codes = None
     w.blocks[13].proj_bias = None
     assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need, None) == NULL
     w.blocks[13].proj_bias = A

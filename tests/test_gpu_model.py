@@ -11,7 +11,7 @@ import oracle as O
 import synth
 import vision_transformer_encoder_amd as vit
 from oracle import inputs as OI
-from gpu_util import announce, assert_close, dev_bf16, host_f64
+from gpu_util import announce, assert_close, check_within, dev_bf16, host_f64, implementation_noise
 
 pytestmark = pytest.mark.gpu
 
@@ -119,63 +119,6 @@ def _gpu_merger(W, m, x_dev, grids):
     y = vit.vit_merge2x2_layernorm(x_dev, grids, t["m_ln_g"], t["m_ln_b"])
     h = vit.vit_bf16_gemm(y, t["m_fc1_w"], bias=t["m_fc1_b"], epilogue=vit.BEPI_BIAS_GELU)
     return vit.vit_bf16_gemm(h, t["m_fc2_w"], bias=t["m_fc2_b"], epilogue=vit.BEPI_BIAS)
-
-
-class implementation_noise:
-    """Context in which the oracle runs with noise of the size of the
-    precision the method's design computes in: half an fp32 ulp (2^-24) on
-    every LayerNorm and GELU output (the quantiser inputs) and half a bf16
-    ulp (2^-8) on every attention probability (the bf16 P of an FA2-style
-    attention, as the FlashRT page's "BF16 attention" does).  The tower amplifies the FP8
-    code flips such noise causes at rounding ties; how far the oracle moves
-    under it is the envelope an fp32/bf16 implementation is held to against
-    the fp64 oracle where it is wider than the stated tolerance."""
-
-    def __init__(self, seed=0):
-        self.rng = np.random.default_rng(seed)
-
-    def _noise(self, y, ulp):
-        return y * (1 + self.rng.choice([-1.0, 1.0], size=y.shape) * ulp)
-
-    def __enter__(self):
-        import math
-        import oracle.vit_oracle as V
-        self.V = V
-        self.orig = (V.layernorm, V.gelu_tanh, V.attention)
-        ln, gelu, _ = self.orig
-        V.layernorm = lambda *a, **k: self._noise(ln(*a, **k), 2.0 ** -24)
-        V.gelu_tanh = lambda *a, **k: self._noise(gelu(*a, **k), 2.0 ** -24)
-
-        def attention(q, k, v, cu_seqlens, num_heads=16, head_dim=72, scale=None):
-            scale = 1.0 / math.sqrt(head_dim) if scale is None else scale
-            out = np.zeros((q.shape[0], num_heads * head_dim))
-            for j in range(len(cu_seqlens) - 1):
-                a, b = int(cu_seqlens[j]), int(cu_seqlens[j + 1])
-                for h in range(num_heads):
-                    sl = slice(h * head_dim, (h + 1) * head_dim)
-                    sc = (q[a:b, sl] @ k[a:b, sl].T) * scale
-                    p = self._noise(np.exp(sc - sc.max(axis=1, keepdims=True)), 2.0 ** -8)
-                    out[a:b, sl] = (p @ v[a:b, sl]) / p.sum(axis=1, keepdims=True)
-            return out
-
-        V.attention = attention
-        return self
-
-    def __exit__(self, *exc):
-        self.V.layernorm, self.V.gelu_tanh, self.V.attention = self.orig
-        return False
-
-
-def check_within(got, ref, env, what):
-    """max_rel <= max(2e-2, 2 * envelope max_rel) and 1 - cos <= max(5e-4,
-    2 * (1 - envelope cos)); both printed."""
-    from gpu_util import metrics
-    rel, cos = metrics(got, ref)
-    erel, ecos = env
-    announce(f"{what}: gpu rel={rel:.3e} cos={cos:.7f} | oracle envelope rel={erel:.3e} cos={ecos:.7f}")
-    assert np.all(np.isfinite(got)), what
-    assert rel <= max(MAX_REL, 2 * erel), f"{what}: rel {rel:.3e}"
-    assert 1 - cos <= max(1 - MIN_COS, 2 * (1 - ecos)), f"{what}: cos {cos:.7f}"
 
 
 def test_encoder_parity_small(gpu, small_tower, oracle_tower):

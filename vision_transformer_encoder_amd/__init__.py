@@ -35,7 +35,7 @@ _ROOT = os.path.dirname(_PKG)
 library_path = os.path.join(_PKG, "libvit.so")
 header_path = os.path.join(_ROOT, "include", "vit.h")
 
-ABI_VERSION = 2  # VIT_ABI_VERSION of the include/vit.h these signatures follow
+ABI_VERSION = 3  # VIT_ABI_VERSION of the include/vit.h these signatures follow
 HIDDEN, HEADS, HEAD_DIM, MLP, MLP_PADDED = 1152, 16, 72, 4304, 4352
 PATCH_DIM, DEPTH, OUT_HIDDEN, MERGED_DIM, NUM_TAPS = 1536, 27, 4096, 4608, 4
 EPI_BIAS, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_FP8 = 0, 1, 2
@@ -63,11 +63,12 @@ class _BlockW(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "ln1_gamma", "ln1_beta", "qkv_codes", "qkv_scales", "qkv_bias", "proj_codes", "proj_scales",
         "proj_bias", "ln2_gamma", "ln2_beta", "fc1_codes", "fc1_scales", "fc1_bias", "fc2_codes",
-        "fc2_scales", "fc2_bias")]
+        "fc2_scales", "fc2_bias", "qkv_w", "proj_w", "fc1_w", "fc2_w")]
 
 
 class _MergerW(ctypes.Structure):
-    _fields_ = [(n, _P) for n in ("ln_gamma", "ln_beta", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
+    _fields_ = [(n, _P) for n in ("ln_gamma", "ln_beta", "fc1_w", "fc1_b", "fc2_w", "fc2_b", "fc1_codes",
+                                  "fc1_scales", "fc2_codes", "fc2_scales")]
 
 
 class _EncoderW(ctypes.Structure):
@@ -81,6 +82,7 @@ _SIGS = {
     "vit_quant_fp8_block128": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P]),
     "vit_e4m3_encode": (_I, [_P, _P, _I64, _P]),
     "vit_layernorm_quant_fp8": (_I, [_P, _I64, _P, _P, _F, _I, _I, _P, _P, _P, _P]),
+    "vit_layernorm": (_I, [_P, _I64, _P, _P, _F, _I, _I, _P, _I64, _P]),
     "vit_fp8_block128_gemm": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
     "vit_bf16_gemm": (_I, [_P, _I, _P, _I, _I, _I, _P, _P, _I, _P, _I64, _P]),
     "vit_rope2d": (_I, [_P, _P, _I64, _P, _I, _I, _I, _F, _P]),
@@ -213,6 +215,15 @@ def vit_layernorm_quant_fp8(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Te
     return (codes, scales, pre) if prequant else (codes, scales)
 
 
+def vit_layernorm(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float = 1e-6,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """LayerNorm of x [M, D] bf16 rows with a bf16 result."""
+    M, D = x.shape
+    out = _out_like(out, (M, D), torch.bfloat16, x.device)
+    _call("vit_layernorm", _p(x), _row_ld(x), _p(gamma), _p(beta), eps, M, D, _p(out), D, _stream(x.device))
+    return out
+
+
 def vit_fp8_block128_gemm(a: torch.Tensor, a_scales: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor,
                           N: int, K: int, bias: Optional[torch.Tensor] = None,
                           residual: Optional[torch.Tensor] = None, epilogue: int = EPI_BIAS,
@@ -323,40 +334,64 @@ def quantize_weight(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
 
 
 class BlockWeights:
-    """Device copy of one block: bf16 norms and biases, FP8 GEMM weights
-    quantised on the GPU with vit_quant_fp8_block128(block_rows=128)."""
+    """Device copy of one block: bf16 norms and biases, and the GEMM weights
+    either quantised on the GPU with vit_quant_fp8_block128(block_rows=128)
+    (precision "fp8") or kept in bf16 (precision "bf16": the block runs its
+    LayerNorms and GEMMs in bf16)."""
 
-    def __init__(self, params: dict, device):
+    def __init__(self, params: dict, device, precision: str = "fp8"):
+        if precision not in ("fp8", "bf16"):
+            raise ValueError("precision is 'fp8' or 'bf16'")
         t = {k: bf16_from_bits(v, device) for k, v in params.items()}
         self.t = t
-        self.q = {n: quantize_weight(t[n + "_w"]) for n in ("qkv", "proj", "fc1", "fc2")}
+        self.precision = precision
+        self.q = {n: quantize_weight(t[n + "_w"]) for n in ("qkv", "proj", "fc1", "fc2")} if precision == "fp8" else {}
         s = _BlockW()
         s.ln1_gamma, s.ln1_beta = _p(t["ln1_g"]), _p(t["ln1_b"])
         s.ln2_gamma, s.ln2_beta = _p(t["ln2_g"]), _p(t["ln2_b"])
         for n in ("qkv", "proj", "fc1", "fc2"):
-            setattr(s, n + "_codes", _p(self.q[n][0]))
-            setattr(s, n + "_scales", _p(self.q[n][1]))
+            if precision == "fp8":
+                setattr(s, n + "_codes", _p(self.q[n][0]))
+                setattr(s, n + "_scales", _p(self.q[n][1]))
+            else:
+                setattr(s, n + "_w", _p(t[n + "_w"]))
             setattr(s, n + "_bias", _p(t[n + "_b"]))
         self.struct = s
 
 
 class MergerWeights:
-    def __init__(self, params: dict, device):
+    """Device copy of one merger: bf16, or (precision "fp8") with its two
+    linears also quantised in 128x128 blocks, which selects the FP8 path."""
+
+    def __init__(self, params: dict, device, precision: str = "bf16"):
+        if precision not in ("fp8", "bf16"):
+            raise ValueError("precision is 'fp8' or 'bf16'")
         t = {k: bf16_from_bits(v, device) for k, v in params.items()}
         self.t = t
+        self.precision = precision
         s = _MergerW()
         s.ln_gamma, s.ln_beta = _p(t["m_ln_g"]), _p(t["m_ln_b"])
         s.fc1_w, s.fc1_b, s.fc2_w, s.fc2_b = _p(t["m_fc1_w"]), _p(t["m_fc1_b"]), _p(t["m_fc2_w"]), _p(t["m_fc2_b"])
+        self.q = {}
+        if precision == "fp8":
+            self.q = {n: quantize_weight(t["m_" + n + "_w"]) for n in ("fc1", "fc2")}
+            s.fc1_codes, s.fc1_scales = _p(self.q["fc1"][0]), _p(self.q["fc1"][1])
+            s.fc2_codes, s.fc2_scales = _p(self.q["fc2"][0]), _p(self.q["fc2"][1])
         self.struct = s
 
 
 class EncoderWeights:
-    def __init__(self, patch: dict, blocks: Sequence[dict], mergers: Sequence[dict], device):
+    def __init__(self, patch: dict, blocks: Sequence[dict], mergers: Sequence[dict], device,
+                 bf16_blocks: int = 0, fp8_mergers: bool = False):
+        """bf16_blocks: the first n blocks run in bf16 (FlashRT keeps 3);
+        fp8_mergers: the mergers run their linears in FP8."""
         if len(blocks) != DEPTH or len(mergers) != NUM_TAPS:
             raise ValueError("the tower has 27 blocks and 4 mergers")
+        if not 0 <= bf16_blocks <= DEPTH:
+            raise ValueError("bf16_blocks is in 0..27")
         self.patch = {k: bf16_from_bits(v, device) for k, v in patch.items()}
-        self.blocks = [BlockWeights(b, device) for b in blocks]
-        self.mergers = [MergerWeights(m, device) for m in mergers]
+        self.blocks = [BlockWeights(b, device, "bf16" if i < bf16_blocks else "fp8") for i, b in enumerate(blocks)]
+        self.mergers = [MergerWeights(m, device, "fp8" if fp8_mergers else "bf16") for m in mergers]
         s = _EncoderW()
         s.patch_w, s.patch_b = _p(self.patch["patch_w"]), _p(self.patch["patch_b"])
         for i, b in enumerate(self.blocks):

@@ -117,33 +117,97 @@ EncoderWs encoder_ws_layout(void* base, int T, int n) {
 }
 
 // ---------------------------------------------------------------- checks
-int check_block_weights(const vit_block_weights* w) {
-  if (!w) return VIT_ERR_NULL;
-  const void* ptrs[] = {w->ln1_gamma, w->ln1_beta, w->qkv_codes, w->qkv_scales, w->qkv_bias,
-                        w->proj_codes, w->proj_scales, w->proj_bias, w->ln2_gamma, w->ln2_beta,
-                        w->fc1_codes, w->fc1_scales, w->fc1_bias, w->fc2_codes, w->fc2_scales,
-                        w->fc2_bias};
-  for (const void* p : ptrs)
+// Pointers of `req` must all be set; of the two optional sets, exactly the
+// one `use_a` selects must be complete (the other is ignored when complete
+// and rejected when partly set).  Every set pointer must be 16-byte aligned.
+template <size_t NR, size_t NA, size_t NB>
+int check_weight_sets(const void* const (&req)[NR], const void* const (&a)[NA], const void* const (&b)[NB],
+                      bool& use_a) {
+  auto count = [](auto& arr) {
+    int n = 0;
+    for (const void* p : arr) n += p != nullptr;
+    return n;
+  };
+  for (const void* p : req)
     if (!p) return VIT_ERR_NULL;
-  for (const void* p : ptrs)
+  const int na = count(a), nb = count(b);
+  if ((na != 0 && na != (int)NA) || (na == 0 && nb != (int)NB)) return VIT_ERR_NULL;
+  use_a = na == (int)NA;
+  for (const void* p : req)
     if (!al16(p)) return VIT_ERR_ALIGN;
+  for (const void* p : a)
+    if (p && !al16(p)) return VIT_ERR_ALIGN;
+  for (const void* p : b)
+    if (p && !al16(p)) return VIT_ERR_ALIGN;
   return VIT_OK;
 }
 
-int check_merger_weights(const vit_merger_weights* m) {
-  const void* ptrs[] = {m->ln_gamma, m->ln_beta, m->fc1_w, m->fc1_b, m->fc2_w, m->fc2_b};
-  for (const void* p : ptrs)
-    if (!p) return VIT_ERR_NULL;
-  for (const void* p : ptrs)
-    if (!al16(p)) return VIT_ERR_ALIGN;
-  return VIT_OK;
+// bf16 is set when the block runs its GEMMs in bf16
+int check_block_weights(const vit_block_weights* w, bool* bf16 = nullptr) {
+  if (!w) return VIT_ERR_NULL;
+  const void* const req[] = {w->ln1_gamma, w->ln1_beta, w->qkv_bias, w->proj_bias,
+                             w->ln2_gamma, w->ln2_beta, w->fc1_bias, w->fc2_bias};
+  const void* const bf[] = {w->qkv_w, w->proj_w, w->fc1_w, w->fc2_w};
+  const void* const f8[] = {w->qkv_codes, w->qkv_scales, w->proj_codes, w->proj_scales,
+                            w->fc1_codes, w->fc1_scales, w->fc2_codes, w->fc2_scales};
+  bool use_bf = false;
+  const int st = check_weight_sets(req, bf, f8, use_bf);
+  if (bf16) *bf16 = use_bf;
+  return st;
+}
+
+// fp8 is set when the merger runs its linears in FP8
+int check_merger_weights(const vit_merger_weights* m, bool* fp8 = nullptr) {
+  const void* const req[] = {m->ln_gamma, m->ln_beta, m->fc1_b, m->fc2_b};
+  const void* const f8[] = {m->fc1_codes, m->fc1_scales, m->fc2_codes, m->fc2_scales};
+  const void* const bf[] = {m->fc1_w, m->fc2_w};
+  bool use_f8 = false;
+  const int st = check_weight_sets(req, f8, bf, use_f8);
+  if (fp8) *fp8 = use_f8;
+  return st;
 }
 
 // ---------------------------------------------------------------- block
+// The bf16-GEMM block (FlashRT section 4: the first 3 blocks stay bf16).
+// Workspace reuse: the LayerNorm outputs [T, 1152] bf16 live in the region
+// of the FP8 activation and hidden codes (unused here), the GELU output
+// [T, 4304] bf16 in the qkv + o regions, dead once proj has read o.
+hipError_t block_forward_bf16_impl(const vit_block_weights* w, uint16_t* x, int T, const int32_t* pos,
+                                   const int32_t* cu_dev, int num_seqs, int64_t attn_work, const BlockWs& ws,
+                                   hipStream_t s) {
+  constexpr int H = VIT_HIDDEN;
+  const size_t t = (size_t)T;
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws.a_codes);
+  uint16_t* h = ws.qkv;
+  if ((size_t)(reinterpret_cast<uint8_t*>(ws.attn_part) - reinterpret_cast<uint8_t*>(ws.qkv)) <
+          t * VIT_MLP * 2 ||
+      (size_t)(reinterpret_cast<uint8_t*>(ws.h_scales) + t * (VIT_MLP_PADDED / 128) * 4 - ws.a_codes) < t * H * 2)
+    return hipErrorInvalidValue;  // the layout no longer has room: a build error, not a caller's
+  hipError_t e;
+  if ((e = vit::launch_layernorm_bf16(x, H, w->ln1_gamma, w->ln1_beta, 1e-6f, T, H, y, H, s)) != hipSuccess)
+    return e;
+  if ((e = vit::launch_bf16_gemm(y, false, w->qkv_w, T, 3 * H, H, w->qkv_bias, nullptr, VIT_BEPI_BIAS, ws.qkv,
+                                 3 * H, s)) != hipSuccess) return e;
+  if ((e = vit::launch_rope2d(ws.qkv, ws.qkv + H, 3 * H, pos, T, VIT_HEADS, VIT_HEAD_DIM, 10000.0f, s)) !=
+      hipSuccess) return e;
+  if ((e = launch_attention(ws.qkv, ws.qkv + H, ws.qkv + 2 * H, 3 * H, ws.o, H, cu_dev, num_seqs, T, attn_work,
+                            VIT_HEADS, 1.0f / std::sqrt((float)VIT_HEAD_DIM), ws.attn_part, s)) != hipSuccess)
+    return e;
+  // x = bf16(x + o W_proj^T + b), in place (each element read before it is written)
+  if ((e = vit::launch_bf16_gemm(ws.o, false, w->proj_w, T, H, H, w->proj_bias, x, VIT_BEPI_BIAS_ADD, x, H, s)) !=
+      hipSuccess) return e;
+  if ((e = vit::launch_layernorm_bf16(x, H, w->ln2_gamma, w->ln2_beta, 1e-6f, T, H, y, H, s)) != hipSuccess)
+    return e;
+  if ((e = vit::launch_bf16_gemm(y, false, w->fc1_w, T, VIT_MLP, H, w->fc1_bias, nullptr, VIT_BEPI_BIAS_GELU, h,
+                                 VIT_MLP, s)) != hipSuccess) return e;
+  return vit::launch_bf16_gemm(h, false, w->fc2_w, T, H, VIT_MLP, w->fc2_bias, x, VIT_BEPI_BIAS_ADD, x, H, s);
+}
+
 hipError_t block_forward_impl(const vit_block_weights* w, uint16_t* x, int T, const int32_t* pos,
                               const int32_t* cu_dev, int num_seqs, int64_t attn_work, const BlockWs& ws,
                               hipStream_t s) {
   constexpr int H = VIT_HIDDEN;
+  if (w->qkv_w) return block_forward_bf16_impl(w, x, T, pos, cu_dev, num_seqs, attn_work, ws, s);
   hipError_t e;
   // LN1 -> FP8 (per token, per 128 columns)
   if ((e = vit::launch_layernorm_quant(x, H, w->ln1_gamma, w->ln1_beta, 1e-6f, T, H, ws.a_codes,
@@ -180,6 +244,19 @@ hipError_t merger_forward_impl(const vit_merger_weights* m, const uint16_t* x, c
   const int TM = T / 4;
   if ((e = vit::launch_merge_layernorm(x, VIT_HIDDEN, grid_dev, n, T, m->ln_gamma, m->ln_beta, 1e-6f,
                                        ws.m_ln, s)) != hipSuccess) return e;
+  if (m->fc1_codes) {
+    // "merger FP8" (FlashRT section 1): the block recipe on the 4608-wide
+    // merged rows.  Codes [T/4, 4608] and scales [T/4, 36] fit the block's
+    // activation and hidden code regions exactly (T/4 * 4608 = T * 1152).
+    const BlockWs& b = ws.blk;
+    if ((e = vit::launch_quant_rows(ws.m_ln, VIT_MERGED_DIM, TM, VIT_MERGED_DIM, b.a_codes, b.a_scales, s)) !=
+        hipSuccess) return e;
+    if ((e = vit::launch_fp8_gemm(b.a_codes, b.a_scales, m->fc1_codes, m->fc1_scales, TM, VIT_MERGED_DIM,
+                                  VIT_MERGED_DIM, m->fc1_b, nullptr, VIT_EPI_BIAS_GELU_FP8, nullptr, b.h_codes,
+                                  b.h_scales, nullptr, s)) != hipSuccess) return e;
+    return vit::launch_fp8_gemm(b.h_codes, b.h_scales, m->fc2_codes, m->fc2_scales, TM, VIT_OUT_HIDDEN,
+                                VIT_MERGED_DIM, m->fc2_b, nullptr, VIT_EPI_BIAS, out, nullptr, nullptr, nullptr, s);
+  }
   if ((e = vit::launch_bf16_gemm(ws.m_ln, false, m->fc1_w, TM, VIT_MERGED_DIM, VIT_MERGED_DIM, m->fc1_b,
                                  nullptr, VIT_BEPI_BIAS_GELU, ws.m_h, VIT_MERGED_DIM, s)) != hipSuccess)
     return e;
@@ -255,6 +332,20 @@ int vit_layernorm_quant_fp8(const uint16_t* x, int64_t ld_x, const uint16_t* gam
     return VIT_ERR_ALIAS;
   return hip_status(vit::launch_layernorm_quant(x, ld_x, gamma, beta, eps, M, D, codes, scales, prequant_debug,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+int vit_layernorm(const uint16_t* x, int64_t ld_x, const uint16_t* gamma, const uint16_t* beta, float eps, int M,
+                  int D, uint16_t* out, int64_t ld_out, vit_stream_t stream) {
+  if (M < 0 || M > kMaxTokens * 4 || D < 128 || D > 8192 || (D % 128) || ld_x < D || ld_out < D)
+    return VIT_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return VIT_ERR_SHAPE;
+  if (M == 0) return VIT_OK;
+  if (!x || !gamma || !beta || !out) return VIT_ERR_NULL;
+  if (!al16(x) || !al16(gamma) || !al16(beta) || !al16(out) || (ld_x & 7) || (ld_out & 7)) return VIT_ERR_ALIGN;
+  const size_t xb = ((size_t)(M - 1) * ld_x + D) * 2, ob = ((size_t)(M - 1) * ld_out + D) * 2;
+  if (overlap(x, xb, out, ob)) return VIT_ERR_ALIAS;
+  return hip_status(vit::launch_layernorm_bf16(x, ld_x, gamma, beta, eps, M, D, out, ld_out,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 int vit_fp8_block128_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,

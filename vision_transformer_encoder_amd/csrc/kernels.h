@@ -16,6 +16,9 @@ hipError_t launch_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStre
 hipError_t launch_layernorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
                                   const uint16_t* beta, float eps, int M, int D, uint8_t* codes,
                                   float* scales, float* prequant, hipStream_t stream);
+// LayerNorm with the normalised row stored in bf16 (same kernel, no quant).
+hipError_t launch_layernorm_bf16(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* beta,
+                                 float eps, int M, int D, uint16_t* out, int64_t ldo, hipStream_t stream);
 
 hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
                            const float* w_scales, int M, int N, int K, const uint16_t* bias,

@@ -109,13 +109,16 @@ __global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restric
 // One wave per row of D = 512*NC or fewer columns (D % 128 == 0).  Chunk
 // i*64+lane holds columns 8*(i*64+lane) .. +8; a 128-column block is 16
 // consecutive chunks, i.e. 16 consecutive lanes of one iteration.
-template <int NC>
+// OUT_BF16: the normalised row is stored in bf16 (out, row stride ldo)
+// instead of being quantised (the bf16-GEMM blocks).
+template <int NC, bool OUT_BF16>
 __global__ __launch_bounds__(256) void layernorm_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                               const uint16_t* __restrict__ gamma,
                                                               const uint16_t* __restrict__ beta, float eps,
                                                               int M, int D, uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales,
-                                                              float* __restrict__ prequant) {
+                                                              float* __restrict__ prequant,
+                                                              uint16_t* __restrict__ out, int64_t ldo) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
@@ -165,6 +168,17 @@ __global__ __launch_bounds__(256) void layernorm_quant_kernel(const uint16_t* __
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = 0.0f;
     }
+    if constexpr (OUT_BF16) {
+      if (live) {
+        uint4 o;
+        o.x = pack_bf16x2(y[0], y[1]);
+        o.y = pack_bf16x2(y[2], y[3]);
+        o.z = pack_bf16x2(y[4], y[5]);
+        o.w = pack_bf16x2(y[6], y[7]);
+        *reinterpret_cast<uint4*>(out + (int64_t)row * ldo + ch * 8) = o;
+      }
+      continue;
+    }
     float am = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(y[j]));
@@ -208,15 +222,16 @@ hipError_t launch_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_layernorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
-                                  const uint16_t* beta, float eps, int M, int D, uint8_t* codes,
-                                  float* scales, float* prequant, hipStream_t stream) {
+template <bool OUT_BF16>
+static hipError_t launch_layernorm(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* beta,
+                                   float eps, int M, int D, uint8_t* codes, float* scales, float* prequant,
+                                   uint16_t* out, int64_t ldo, hipStream_t stream) {
   const int nc = (D / 8 + 63) / 64;
   const dim3 grid((M + 3) / 4), block(256);
-#define VIT_LNQ_CASE(N)                                                                             \
-  case N:                                                                                          \
-    layernorm_quant_kernel<N><<<grid, block, 0, stream>>>(x, ldx, gamma, beta, eps, M, D, codes, \
-                                                          scales, prequant);                      \
+#define VIT_LNQ_CASE(N)                                                                               \
+  case N:                                                                                            \
+    layernorm_quant_kernel<N, OUT_BF16><<<grid, block, 0, stream>>>(x, ldx, gamma, beta, eps, M, D, \
+                                                                    codes, scales, prequant, out, ldo); \
     break;
   switch (nc) {
     VIT_LNQ_CASE(1)
@@ -240,6 +255,17 @@ hipError_t launch_layernorm_quant(const uint16_t* x, int64_t ldx, const uint16_t
   }
 #undef VIT_LNQ_CASE
   return hipGetLastError();
+}
+
+hipError_t launch_layernorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
+                                  const uint16_t* beta, float eps, int M, int D, uint8_t* codes,
+                                  float* scales, float* prequant, hipStream_t stream) {
+  return launch_layernorm<false>(x, ldx, gamma, beta, eps, M, D, codes, scales, prequant, nullptr, 0, stream);
+}
+
+hipError_t launch_layernorm_bf16(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* beta,
+                                 float eps, int M, int D, uint16_t* out, int64_t ldo, hipStream_t stream) {
+  return launch_layernorm<true>(x, ldx, gamma, beta, eps, M, D, nullptr, nullptr, nullptr, out, ldo, stream);
 }
 
 }  // namespace vit
