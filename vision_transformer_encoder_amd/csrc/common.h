@@ -83,6 +83,21 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
   return x * q + min(x, r) + i;
 }
 
+// Output tile (m_tile, n_tile) of logical tile index lb when the n tiles are
+// walked in groups of group_n: every m tile of one group, then the next
+// group.  With XCD-contiguous logical indices, the workgroups resident on
+// one XCD at a time then share one group's weight slice in its L2 instead
+// of streaming the whole weight.  group_n >= n_tiles is plain m-major order.
+__device__ __forceinline__ void grouped_tile(int lb, int m_tiles, int n_tiles, int group_n, int& m_tile,
+                                             int& n_tile) {
+  const int g = lb / (m_tiles * group_n);
+  const int n0 = g * group_n;
+  const int gn = min(group_n, n_tiles - n0);
+  const int rem = lb - g * m_tiles * group_n;
+  m_tile = rem / gn;
+  n_tile = n0 + rem % gn;
+}
+
 // tanh-form GELU in fp32, evaluated through the identity
 // 0.5 x (1 + tanh(u)) = x / (1 + e^(-2u)),  u = sqrt(2/pi) (x + 0.044715 x^3):
 // one exp2 and one reciprocal instead of a tanh, and no cancellation in

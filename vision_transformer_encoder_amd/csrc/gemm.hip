@@ -74,7 +74,7 @@ __device__ __forceinline__ void park_acc(float* c_lds, const f32x16_t acc[2][2],
 template <int EPI>
 __global__ __launch_bounds__(256) void fp8_gemm_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ a_scales, const uint8_t* __restrict__ w,
-    const float* __restrict__ w_scales, int M, int N, int Np, int Kp, int n_tiles, int nblocks,
+    const float* __restrict__ w_scales, int M, int N, int Np, int Kp, int n_tiles, int nblocks, int group_n,
     const uint16_t* __restrict__ bias, const uint16_t* residual, uint16_t* out,
     uint8_t* __restrict__ out_codes, float* __restrict__ out_scales, float* __restrict__ prequant) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileB];  // A x2, W x2; C tile after the loop
@@ -86,7 +86,8 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
   const int wn = wave & 1, wm = wave >> 1;
   const int l32 = lane & 31, g = lane >> 5;
   const int lb = xcd_logical_block(blockIdx.x, nblocks);
-  const int m_tile = lb / n_tiles, n_tile = lb % n_tiles;
+  int m_tile, n_tile;
+  grouped_tile(lb, nblocks / n_tiles, n_tiles, group_n, m_tile, n_tile);
   const int n0 = n_tile * kBN, m0 = m_tile * kBM;
   const int Kb = Kp >> 7;
 
@@ -258,6 +259,17 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
   }
 }
 
+// n tiles per group of the tile order (grouped_tile): groups of at most
+// kGroupN tiles, of near-equal size
+#ifndef VIT_GEMM_GROUP
+#define VIT_GEMM_GROUP 12
+#endif
+static int gemm_group_n(int n_tiles) {
+  if (VIT_GEMM_GROUP <= 0) return n_tiles;
+  const int groups = (n_tiles + VIT_GEMM_GROUP - 1) / VIT_GEMM_GROUP;
+  return (n_tiles + groups - 1) / groups;
+}
+
 hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
                            const float* w_scales, int M, int N, int K, const uint16_t* bias,
                            const uint16_t* residual, int epilogue, uint16_t* out,
@@ -272,15 +284,18 @@ hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_scales, const uint8_
   switch (epilogue) {
     case 0:
       fp8_gemm_kernel<0><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks,
-                                                   bias, residual, out, out_codes, out_scales, prequant);
+                                                   gemm_group_n(n_tiles), bias, residual, out, out_codes,
+                                                   out_scales, prequant);
       break;
     case 1:
       fp8_gemm_kernel<1><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks,
-                                                   bias, residual, out, out_codes, out_scales, prequant);
+                                                   gemm_group_n(n_tiles), bias, residual, out, out_codes,
+                                                   out_scales, prequant);
       break;
     case 2:
       fp8_gemm_kernel<2><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks,
-                                                   bias, residual, out, out_codes, out_scales, prequant);
+                                                   gemm_group_n(n_tiles), bias, residual, out, out_codes,
+                                                   out_scales, prequant);
       break;
     default:
       return hipErrorInvalidValue;
@@ -295,7 +310,7 @@ hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_scales, const uint8_
 template <int EPI, bool A_F32>
 __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__ a_ptr,
                                                         const uint16_t* __restrict__ w, int M, int N,
-                                                        int K, int n_tiles, int nblocks,
+                                                        int K, int n_tiles, int nblocks, int group_n,
                                                         const uint16_t* __restrict__ bias,
                                                         const uint16_t* __restrict__ add,
                                                         uint16_t* __restrict__ out, int64_t ld_out) {
@@ -307,7 +322,8 @@ __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__
   const int wn = wave & 1, wm = wave >> 1;
   const int l32 = lane & 31, g = lane >> 5;
   const int lb = xcd_logical_block(blockIdx.x, nblocks);
-  const int m_tile = lb / n_tiles, n_tile = lb % n_tiles;
+  int m_tile, n_tile;
+  grouped_tile(lb, nblocks / n_tiles, n_tiles, group_n, m_tile, n_tile);
   const int n0 = n_tile * kBN, m0 = m_tile * kBM;
   const int ksteps = (K + 63) / 64;
 
@@ -454,7 +470,8 @@ hipError_t launch_bf16_gemm(const void* a, bool a_f32, const uint16_t* w, int M,
   const int nblocks = n_tiles * m_tiles;
   const dim3 grid(nblocks);
 #define VIT_BG(E, F)                                                                                        \
-  bf16_gemm_kernel<E, F><<<grid, 256, 0, stream>>>(a, w, M, N, K, n_tiles, nblocks, bias, add, out, ld_out)
+  bf16_gemm_kernel<E, F><<<grid, 256, 0, stream>>>(a, w, M, N, K, n_tiles, nblocks, gemm_group_n(n_tiles), bias, \
+                                                   add, out, ld_out)
   if (a_f32) {
     switch (epilogue) {
       case 0: VIT_BG(0, true); break;
