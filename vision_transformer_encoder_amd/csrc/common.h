@@ -67,6 +67,22 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 // max over aligned groups of 16 lanes
+// Max over each row of 16 lanes (the rows of DPP), left in every lane of the
+// row: quad swaps (xor 1, xor 2), then the half-row and row mirrors.  VALU
+// only, no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_fmax(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __builtin_bit_cast(float, o));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = dpp_fmax<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_fmax<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_fmax<0x141>(v);  // row_half_mirror
+  v = dpp_fmax<0x140>(v);  // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ float group16_max(float v) {
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -70,6 +70,11 @@ __device__ __forceinline__ void park_acc(float* c_lds, const f32x16_t acc[2][2],
   }
 }
 
+// Workgroup barrier over LDS only: this wave's LDS traffic is complete; its
+// global loads in flight are not waited for (their registers are tracked by
+// the compiler as usual).
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ============================================================ FP8 block-128
 template <int EPI>
 __global__ __launch_bounds__(256) void fp8_gemm_kernel(
@@ -180,38 +185,58 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
   }
 
   // ---------------------------------------------------------------- epilogue
-  float* c_lds = reinterpret_cast<float*>(smem);
-  park_acc(c_lds, acc, wn, wm, l32, g);
-  __syncthreads();
-  // thread -> (row = tid/16 + 16 pass, 8 columns at (tid%16)*8)
+  // thread -> (row = tid/16 + 16 pass, 8 columns at (tid%16)*8).  The bias
+  // and residual loads are issued before the tile is parked, so their
+  // latency overlaps the LDS round trip, and all eight rows are read from
+  // LDS before the first is finished.
   const int cc = (tid & 15) * 8;
   const int n = n0 + cc;
+  const bool vec = n + 8 <= N && (N & 7) == 0;
   float b8[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) b8[j] = 0.0f;
   if (bias) {
-    if (n + 8 <= N && (N & 7) == 0) {
+    if (vec) {
       load8_bf16(bias, n, N, b8);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) b8[j] = (n + j < N) ? bf2f(bias[n + j]) : 0.0f;
     }
   }
-#pragma unroll 2
+  uint4 res8[8];
+  if constexpr (EPI == 1) {
+    if (vec) {
+#pragma unroll
+      for (int pass = 0; pass < 8; ++pass) {
+        const int m = min(m0 + (tid >> 4) + 16 * pass, M - 1);
+        res8[pass] = *reinterpret_cast<const uint4*>(residual + (int64_t)m * N + n);
+      }
+    }
+  }
+  float* c_lds = reinterpret_cast<float*>(smem);
+  park_acc(c_lds, acc, wn, wm, l32, g);
+  tile_barrier();
+  float4 cv[8][2];
+#pragma unroll
   for (int pass = 0; pass < 8; ++pass) {
     const int ml = (tid >> 4) + 16 * pass;
-    const int m = m0 + ml;
-    const float4 c0 = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc);
-    const float4 c1 = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc + 4);
+    cv[pass][0] = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc);
+    cv[pass][1] = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc + 4);
+  }
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int m = m0 + (tid >> 4) + 16 * pass;
+    const float4 c0 = cv[pass][0], c1 = cv[pass][1];
     float y[8] = {c0.x + b8[0], c0.y + b8[1], c0.z + b8[2], c0.w + b8[3],
                   c1.x + b8[4], c1.y + b8[5], c1.z + b8[6], c1.w + b8[7]};
     if constexpr (EPI == 0 || EPI == 1) {
       if (m < M) {
-        const bool vec = n + 8 <= N && (N & 7) == 0;
         if constexpr (EPI == 1) {
           float r8[8];
           if (vec) {
-            load8_bf16(residual + (int64_t)m * N, n, N, r8);
+            const uint4 w4 = res8[pass];
+            r8[0] = bf_lo(w4.x); r8[1] = bf_hi(w4.x); r8[2] = bf_lo(w4.y); r8[3] = bf_hi(w4.y);
+            r8[4] = bf_lo(w4.z); r8[5] = bf_hi(w4.z); r8[6] = bf_lo(w4.w); r8[7] = bf_hi(w4.w);
           } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) r8[j] = (n + j < N) ? bf2f(residual[(int64_t)m * N + n + j]) : 0.0f;
@@ -233,14 +258,16 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
         }
       }
     } else {
-      // GELU, then FP8 requant of this row's 128 columns (16 lanes x 8)
+      // GELU, then FP8 requant of this row's 128 columns (16 lanes x 8);
+      // columns past N are zero
       float am = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        y[j] = (n + j < N) ? gelu_tanh(y[j]) : 0.0f;
+        const float gj = gelu_tanh(y[j]);
+        y[j] = (n + j < N) ? gj : 0.0f;
         am = fmaxf(am, fabsf(y[j]));
       }
-      am = group16_max(am);
+      am = row16_max(am);
       float s, inv;
       block_scale(am, s, inv);
       if (m < M) {
