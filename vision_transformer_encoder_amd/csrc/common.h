@@ -56,37 +56,47 @@ __device__ __forceinline__ void block_scale(float amax, float& s, float& inv) {
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// Cross-lane reductions without LDS round trips.  A row of 16 lanes is
+// reduced with DPP (quad swaps xor 1 and xor 2, then the half-row and row
+// mirrors); rows are then combined with the 16- and 32-lane swaps, whose
+// result pair holds the lane's own value and its partner's.  Every step adds
+// the same two values in every lane that receives them (a + b = b + a), so
+// the result is bit-identical across the lanes it covers.
+template <int CTRL>
+__device__ __forceinline__ float dpp_peer(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+// max over each row of 16 lanes, in every lane of the row
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_peer<kDppXor1>(v));
+  v = fmaxf(v, dpp_peer<kDppXor2>(v));
+  v = fmaxf(v, dpp_peer<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_peer<kDppMirror>(v));
   return v;
+}
+__device__ __forceinline__ float group16_max(float v) { return row16_max(v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_peer<kDppXor1>(v);
+  v += dpp_peer<kDppXor2>(v);
+  v += dpp_peer<kDppHalfMirror>(v);
+  v += dpp_peer<kDppMirror>(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = __int_as_float(r16[0]) + __int_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(r32[0]) + __int_as_float(r32[1]);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-// max over aligned groups of 16 lanes
-// Max over each row of 16 lanes (the rows of DPP), left in every lane of the
-// row: quad swaps (xor 1, xor 2), then the half-row and row mirrors.  VALU
-// only, no LDS round trips.
-template <int CTRL>
-__device__ __forceinline__ float dpp_fmax(float v) {
-  const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
-  return fmaxf(v, __builtin_bit_cast(float, o));
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = dpp_fmax<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_fmax<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_fmax<0x141>(v);  // row_half_mirror
-  v = dpp_fmax<0x140>(v);  // row_mirror
-  return v;
-}
-
-__device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = row16_max(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = fmaxf(__int_as_float(r16[0]), __int_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(r32[0]), __int_as_float(r32[1]));
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  Logical index
