@@ -21,11 +21,15 @@ def _qkv_bits(cfg, T, seed=0):
     return [synth.normal_bf16(cfg, t, seed, (T, 1152)) for t in ("q", "k", "v")]
 
 
-@pytest.mark.parametrize("grids", [[(48, 38)], [(18, 54), (36, 108), (24, 76)]], ids=["48x38", "varlen3"])
-def test_rope2d(gpu, grids):
+# row stride 3456 takes the staged 16-byte path; 3460 (rows not 16-byte
+# aligned) the one-lane-per-unit path
+@pytest.mark.parametrize("ld", [3456, 3460])
+@pytest.mark.parametrize("grids", [[(48, 38)], [(18, 54), (36, 108), (24, 76)], [(3, 5)]],
+                         ids=["48x38", "varlen3", "3x5"])
+def test_rope2d(gpu, grids, ld):
     T = sum(h * w for h, w in grids)
     q, k, _ = _qkv_bits(1, T)
-    qkv = torch.zeros((T, 3456), dtype=torch.bfloat16, device=gpu)
+    qkv = torch.zeros((T, ld), dtype=torch.bfloat16, device=gpu)
     qkv[:, :1152] = dev_bf16(q, gpu)
     qkv[:, 1152:2304] = dev_bf16(k, gpu)
     pos = synth.positions(grids)
