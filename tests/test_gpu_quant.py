@@ -46,7 +46,7 @@ def test_e4m3_encoder_decision_points(gpu):
     assert codes[np.nonzero((x == 0) & np.signbit(x))[0][0]] == 0x80
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 128), (7, 200), (300, 1152), (6256, 1152)])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (7, 200), (300, 1152), (6256, 1152), (5, 4608), (3, 9000)])
 def test_quant_rows_bit_exact(gpu, rows, cols):
     bits = synth.normal_bf16(2, "a", rows * 7 + cols, (rows, cols))
     bits[:, :3] = 0  # some structure: zero columns
