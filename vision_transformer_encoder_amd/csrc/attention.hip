@@ -613,7 +613,13 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams a) {
 // block of the range that holds an item's last key tile does it, reading the
 // item's segments in key order (deterministic):
 //   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  O = sum_s 2^(m_s - m) O_s / l.
+// Thread (query, half) merges 36 of the query's 72 values; the bf16 tile is
+// parked in LDS and written back as whole 144-byte head rows, 16 bytes per
+// lane on consecutive lanes.
 __global__ __launch_bounds__(2 * kBQ) void attention_combine_kernel(AttnParams a) {
+  constexpr int kHalf = kHD / 2;
+  constexpr int kRowU4 = kHD / 8;  // 16-byte chunks per query row (9)
+  __shared__ uint4 tile[kBQ * kRowU4];
   const int lg = blockIdx.x;  // range
   const int64_t p = range_start(a, lg), end = range_start(a, lg + 1);
   if (p >= end) return;
@@ -625,33 +631,39 @@ __global__ __launch_bounds__(2 * kBQ) void attention_combine_kernel(AttnParams a
   while (g0 > 0 && range_start(a, g0) > p0) --g0;
 
   const int tid = threadIdx.x, qi = tid & (kBQ - 1), half = tid / kBQ;
-  const int q_local = s.qtile * kBQ + qi;
-  if (q_local >= s.seq_len) return;
-  auto slot_of = [&](int gg) -> const float* {
-    return a.partial + (size_t)(gg == g0 ? 2 * gg + 1 : 2 * gg) * kSlotFloats;
-  };
-  float m = -INFINITY;
-  for (int gg = g0; gg <= lg; ++gg) m = fmaxf(m, slot_of(gg)[(kHD + 1) * kBQ + qi]);
-  constexpr int kHalf = kHD / 2;
-  float o[kHalf];
+  const int rows = min(kBQ, s.seq_len - s.qtile * kBQ);  // queries of this tile inside the window
+  if (qi < rows) {
+    auto slot_of = [&](int gg) -> const float* {
+      return a.partial + (size_t)(gg == g0 ? 2 * gg + 1 : 2 * gg) * kSlotFloats;
+    };
+    float m = -INFINITY;
+    for (int gg = g0; gg <= lg; ++gg) m = fmaxf(m, slot_of(gg)[(kHD + 1) * kBQ + qi]);
+    float o[kHalf];
 #pragma unroll
-  for (int i = 0; i < kHalf; ++i) o[i] = 0.0f;
-  float l = 0.0f;
-  for (int gg = g0; gg <= lg; ++gg) {
-    const float* sl = slot_of(gg);
-    const float w = __builtin_amdgcn_exp2f(sl[(kHD + 1) * kBQ + qi] - m);
-    l = fmaf(w, sl[kHD * kBQ + qi], l);
+    for (int i = 0; i < kHalf; ++i) o[i] = 0.0f;
+    float l = 0.0f;
+    for (int gg = g0; gg <= lg; ++gg) {
+      const float* sl = slot_of(gg);
+      const float w = __builtin_amdgcn_exp2f(sl[(kHD + 1) * kBQ + qi] - m);
+      l = fmaf(w, sl[kHD * kBQ + qi], l);
 #pragma unroll
-    for (int i = 0; i < kHalf; ++i) o[i] = fmaf(w, sl[(half * kHalf + i) * kBQ + qi], o[i]);
+      for (int i = 0; i < kHalf; ++i) o[i] = fmaf(w, sl[(half * kHalf + i) * kBQ + qi], o[i]);
+    }
+    const float inv_l = 1.0f / l;
+    uint2* trow = reinterpret_cast<uint2*>(tile + qi * kRowU4) + half * (kHalf / 4);
+#pragma unroll
+    for (int i = 0; i < kHalf; i += 4) {
+      uint2 w;
+      w.x = pack_bf16x2(o[i] * inv_l, o[i + 1] * inv_l);
+      w.y = pack_bf16x2(o[i + 2] * inv_l, o[i + 3] * inv_l);
+      trow[i / 4] = w;
+    }
   }
-  const float inv_l = 1.0f / l;
-  uint16_t* op = a.o + (int64_t)(s.seq_begin + q_local) * a.ldo + (int64_t)s.head * kHD + half * kHalf;
-#pragma unroll
-  for (int i = 0; i < kHalf; i += 4) {
-    uint2 w;
-    w.x = pack_bf16x2(o[i] * inv_l, o[i + 1] * inv_l);
-    w.y = pack_bf16x2(o[i + 2] * inv_l, o[i + 3] * inv_l);
-    *reinterpret_cast<uint2*>(op + i) = w;
+  __syncthreads();
+  uint16_t* obase = a.o + (int64_t)(s.seq_begin + s.qtile * kBQ) * a.ldo + (int64_t)s.head * kHD;
+  for (int c = tid; c < rows * kRowU4; c += 2 * kBQ) {
+    const int q = c / kRowU4, ch = c - q * kRowU4;
+    *reinterpret_cast<uint4*>(obase + (int64_t)q * a.ldo + ch * 8) = tile[c];
   }
 }
 

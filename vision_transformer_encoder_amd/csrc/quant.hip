@@ -13,11 +13,7 @@
 namespace vit {
 
 // ---------------------------------------------------------------- per row
-// One wave per row.  Lane l holds the 8-column chunks l, l + 64, ... (NC of
-// them); a 128-column block is 16 consecutive chunks, i.e. 16 consecutive
-// lanes of one chunk slot.  Every load of the row is issued before the first
-// block is finished.
-template <int NC>
+// One wave per row; blocks of 128 columns, four per wave iteration.
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                          int rows, int cols, int Cp,
                                                          uint8_t* __restrict__ codes,
@@ -26,68 +22,29 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const uint16_t* xr = x + (int64_t)row * ldx;
-  const int nchunk = Cp >> 3, nblk = Cp >> 7;
-  float v[NC][8];
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int ch = i * 64 + lane;
-    if (ch < nchunk) {
-      load8_bf16(xr, ch * 8, cols, v[i]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int ch = i * 64 + lane;
-    float am = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[i][j]));
-    am = row16_max(am);
-    float s, inv;
-    block_scale(am, s, inv);
-    if (ch < nchunk) {
-      uint2 o;
-      o.x = e4m3x4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
-      o.y = e4m3x4(v[i][4] * inv, v[i][5] * inv, v[i][6] * inv, v[i][7] * inv);
-      *reinterpret_cast<uint2*>(codes + (int64_t)row * Cp + ch * 8) = o;
-      if ((lane & 15) == 0) scales[(int64_t)row * nblk + (ch >> 4)] = s;
-    }
-  }
-}
-
-// Rows wider than 8192 columns: the same mapping, one 64-chunk slot at a time.
-__global__ __launch_bounds__(256) void quant_rows_wide_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                              int rows, int cols, int Cp,
-                                                              uint8_t* __restrict__ codes,
-                                                              float* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const uint16_t* xr = x + (int64_t)row * ldx;
-  const int nchunk = Cp >> 3, nblk = Cp >> 7;
-  for (int c0 = 0; c0 < nchunk; c0 += 64) {
-    const int ch = c0 + lane;
+  const int nblk = Cp >> 7;
+  for (int b0 = 0; b0 < nblk; b0 += 4) {
+    const int b = b0 + (lane >> 4);
+    const int c = b * 128 + (lane & 15) * 8;
     float v[8];
-    if (ch < nchunk) {
-      load8_bf16(xr, ch * 8, cols, v);
+    if (b < nblk) {
+      load8_bf16(xr, c, cols, v);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
     float am = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
-    am = row16_max(am);
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = group16_max(am);
     float s, inv;
     block_scale(am, s, inv);
-    if (ch < nchunk) {
+    if (b < nblk) {
       uint2 o;
       o.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
       o.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-      *reinterpret_cast<uint2*>(codes + (int64_t)row * Cp + ch * 8) = o;
-      if ((lane & 15) == 0) scales[(int64_t)row * nblk + (ch >> 4)] = s;
+      *reinterpret_cast<uint2*>(codes + (int64_t)row * Cp + c) = o;
+      if ((lane & 15) == 0) scales[(int64_t)row * nblk + b] = s;
     }
   }
 }
@@ -247,33 +204,7 @@ __global__ __launch_bounds__(256) void layernorm_quant_kernel(const uint16_t* __
 hipError_t launch_quant_rows(const uint16_t* x, int64_t ldx, int rows, int cols, uint8_t* codes,
                              float* scales, hipStream_t stream) {
   const int Cp = (cols + 127) / 128 * 128;
-  const int nc = (Cp / 8 + 63) / 64;
-  const dim3 grid((rows + 3) / 4), block(256);
-#define VIT_QR_CASE(N)                                                                         \
-  case N:                                                                                      \
-    quant_rows_kernel<N><<<grid, block, 0, stream>>>(x, ldx, rows, cols, Cp, codes, scales); \
-    break;
-  switch (nc) {
-    VIT_QR_CASE(1)
-    VIT_QR_CASE(2)
-    VIT_QR_CASE(3)
-    VIT_QR_CASE(4)
-    VIT_QR_CASE(5)
-    VIT_QR_CASE(6)
-    VIT_QR_CASE(7)
-    VIT_QR_CASE(8)
-    VIT_QR_CASE(9)
-    VIT_QR_CASE(10)
-    VIT_QR_CASE(11)
-    VIT_QR_CASE(12)
-    VIT_QR_CASE(13)
-    VIT_QR_CASE(14)
-    VIT_QR_CASE(15)
-    VIT_QR_CASE(16)
-    default:
-      quant_rows_wide_kernel<<<grid, block, 0, stream>>>(x, ldx, rows, cols, Cp, codes, scales);
-  }
-#undef VIT_QR_CASE
+  quant_rows_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(x, ldx, rows, cols, Cp, codes, scales);
   return hipGetLastError();
 }
 
