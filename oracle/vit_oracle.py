@@ -569,6 +569,62 @@ def patch_embed(pixels, w: EncoderWeights, pos_embed=None, mode: str = "storage"
     return _rb(c, mode == "storage")
 
 
+# Learned position table: num_grid_per_side = 48, i.e. [2304, 1152]
+# (spark_model page, struct VisionEncoder fields pos_embed and
+# num_grid_per_side).
+POS_GRID = 48
+
+
+def pos_embed_interp(table, grids: Sequence[Tuple[int, int]], grid_side: int = POS_GRID) -> np.ndarray:
+    """Per-token position embedding resampled from the learned [G*G, D] table
+    (FlashRT section 3, "patch_embed -> +interpolated pos_embed"; spark_model
+    page, struct VisionEncoder: a [2304, 1152] bf16 table with
+    num_grid_per_side 48, kept on the host as f32 for the per-prompt
+    geometry).  Returns [T, D] bf16 values, tokens in raster order per image,
+    images packed in order.
+
+    The pages do not state the resampling rule.  Reading taken: bilinear
+    interpolation with corner-aligned samples, in f32 arithmetic (the page's
+    host copy is f32), each operation rounded to f32 in this order:
+      y = ((G-1) r) / (h-1) (0 when h = 1), y0 = floor(y), y1 = min(y0+1, G-1),
+      dy = y - y0, and the same along the columns (x, x0, x1, dx);
+      w00 = (1-dy)(1-dx), w01 = (1-dy) dx, w10 = dy (1-dx), w11 = dy dx;
+      v = ((w00 T[y0,x0] + w01 T[y0,x1]) + w10 T[y1,x0]) + w11 T[y1,x1],
+    then v is stored as bf16 (the operand the patch embedding adds)."""
+    G = int(grid_side)
+    tab = np.asarray(table, dtype=np.float64)
+    if tab.ndim != 2 or tab.shape[0] != G * G:
+        raise ValueError("table must be [G*G, D]")
+    t32 = tab.astype(np.float32)
+    if not np.array_equal(t32.astype(np.float64), tab):
+        raise ValueError("table values must be f32 (bf16) values")
+    f = np.float32
+    out = []
+    for h, w in grids:
+        def axis(n):
+            i = np.arange(n, dtype=np.float32)
+            y = (f(G - 1) * i) / f(n - 1) if n > 1 else np.zeros(n, dtype=np.float32)
+            y0 = np.floor(y).astype(np.int64)
+            y1 = np.minimum(y0 + 1, G - 1)
+            return y0, y1, (y - y0.astype(np.float32)).astype(np.float32)
+        y0, y1, dy = axis(h)
+        x0, x1, dx = axis(w)
+        dy, dx = dy[:, None], dx[None, :]
+        one = f(1.0)
+        w00 = ((one - dy) * (one - dx))[..., None]
+        w01 = ((one - dy) * dx)[..., None]
+        w10 = (dy * (one - dx))[..., None]
+        w11 = (dy * dx)[..., None]
+        t00 = t32[(y0[:, None] * G + x0[None, :])]
+        t01 = t32[(y0[:, None] * G + x1[None, :])]
+        t10 = t32[(y1[:, None] * G + x0[None, :])]
+        t11 = t32[(y1[:, None] * G + x1[None, :])]
+        v = ((w00 * t00 + w01 * t01) + w10 * t10) + w11 * t11
+        assert v.dtype == np.float32
+        out.append(v.reshape(h * w, -1).astype(np.float64))
+    return bf16(np.concatenate(out, axis=0))
+
+
 def encoder_forward(pixels, w: EncoderWeights, grids, pos_embed=None,
                     mode: str = "storage", depth: int = DEPTH,
                     taps: Sequence[int] = TAPS, trace: Optional[dict] = None,
