@@ -133,6 +133,8 @@ def main() -> int:
     ap.add_argument("--bf16-blocks", type=int, default=0,
                     help="precision variant: the first N blocks run LayerNorm and GEMMs in bf16 (the pages keep 3)")
     ap.add_argument("--fp8-mergers", action="store_true", help="precision variant: FP8 merger linears")
+    ap.add_argument("--pos-table", action="store_true",
+                    help="add the learned 48x48 position table, resampled to the grid, after the patch embedding")
     ap.add_argument("--graph", action="store_true",
                     help="capture the whole forward once as a HIP graph and time its replays")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -169,9 +171,10 @@ def main() -> int:
         print(json.dumps({"kernel": args.kernel, "workload": args.workload, **k[args.kernel]}), flush=True)
         return 0
     ep = synth.encoder_params(cfg)
+    pos_table = synth.normal_bf16(cfg, "pos_table", 48, (48 * 48, 1152), std=0.02) if args.pos_table else None
     W = vit.EncoderWeights(ep.patch, ep.blocks, ep.mergers, dev, bf16_blocks=args.bf16_blocks,
-                           fp8_mergers=args.fp8_mergers)
-    variant = args.bf16_blocks > 0 or args.fp8_mergers
+                           fp8_mergers=args.fp8_mergers, pos_table=pos_table)
+    variant = args.bf16_blocks > 0 or args.fp8_mergers or args.pos_table
     if variant:
         args.no_kernels = True  # the per-kernel timing replays the all-FP8 block sequence
     px = torch.from_numpy(synth.pixels(cfg, T)).to(dev)
@@ -253,6 +256,7 @@ def main() -> int:
         "outputs_finite": ok,
         "launch": "hip_graph" if args.graph else "eager",
         "precision": {"bf16_blocks": args.bf16_blocks, "fp8_mergers": bool(args.fp8_mergers)},
+        "position_table": "learned 48x48, resampled per image" if args.pos_table else None,
     }
     if roofline is not None:
         line["roofline"] = roofline
@@ -416,6 +420,8 @@ def time_kernels(vit, W, T, grids, dev, reps, seq, only=None, eager=False):
     mo = torch.empty((TM, 4096), dtype=torch.bfloat16, device=dev)
     px = torch.rand((T, 1536), device=dev) * 2 - 1
     xp = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ptab = torch.randn((48 * 48, H), device=dev).to(torch.bfloat16)
+    pe_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     cpy_src = torch.randn((T, 4096), device=dev).to(torch.bfloat16)
     cpy_dst = torch.empty_like(cpy_src)
     att_flop = sum(4 * p * p * H for p in seq)
@@ -453,6 +459,10 @@ def time_kernels(vit, W, T, grids, dev, reps, seq, only=None, eager=False):
         "merger_fc2_bf16": (lambda: vit.vit_bf16_gemm(mh, m["m_fc2_w"], bias=m["m_fc2_b"], out=mo),
                             2 * TM * 4096 * 4608, "F16", 4),
     }
+    # the learned position table resampled to the grids (only with --pos-table
+    # in the forward): the table read once, the [T, 1152] result written
+    cases["pos_embed_interp"] = (lambda: vit.vit_pos_embed_interp(ptab, grids, out=pe_out),
+                                 48 * 48 * H * 2 + T * H * 2, "B", 0)
     # a plain copy of known size: the reference for the HBM byte counters
     cases["copy_calibration"] = (lambda: cpy_dst.copy_(cpy_src), 2 * cpy_src.numel() * 2, "B", 0)
     res = {}

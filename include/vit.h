@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define VIT_ABI_VERSION 3
+#define VIT_ABI_VERSION 4
 
 /* Model dimensions (FlashRT section 3; spark_model struct VisionEncoder). */
 #define VIT_HIDDEN 1152
@@ -237,6 +237,30 @@ int vit_merge2x2_layernorm(const uint16_t* x, int D, const int32_t* grid_hw_dev,
                            uint16_t* out, vit_stream_t stream);
 
 /* ---------------------------------------------------------------------
+ * Learned position embedding resampled to each image's patch grid
+ * (FlashRT section 3: "patch_embed -> +interpolated pos_embed"; spark_model
+ * struct VisionEncoder: a [G*G, 1152] bf16 table with num_grid_per_side
+ * G = 48).  The pages do not give the rule; this computes corner-aligned
+ * bilinear samples: token (r, c) of an h x w image reads the table at
+ * y = (G-1) r / (h-1), x = (G-1) c / (w-1) (0 for a single row / column),
+ * in f32 with each operation rounded in the order
+ *   ((w00 T[y0,x0] + w01 T[y0,x1]) + w10 T[y1,x0]) + w11 T[y1,x1],
+ * w00 = (1-dy)(1-dx), w01 = (1-dy) dx, w10 = dy (1-dx), w11 = dy dx, and
+ * stores bf16.
+ * table: [G*G, dim] bf16 (1 <= G <= 1024, dim % 8 == 0).  grid_hw_dev /
+ * grid_hw_host: [num_images, 2] int32 (h, w >= 1, sum h*w == T), tokens in
+ * raster order per image, images packed in order.  out: [T, ld_out] bf16
+ * (ld_out >= dim, ld_out % 8 == 0), written in columns [0, dim).
+ * Errors: SHAPE for out-of-range sizes, SEQLENS for grids that do not
+ * sum to T, NULL / ALIGN (16-byte pointers) / ALIAS (out overlapping the
+ * table or the grids); nothing is enqueued on error.
+ * ------------------------------------------------------------------- */
+int vit_pos_embed_interp(const uint16_t* table, int grid_side, int dim,
+                         const int32_t* grid_hw_dev, const int32_t* grid_hw_host,
+                         int num_images, int T, uint16_t* out, int64_t ld_out,
+                         vit_stream_t stream);
+
+/* ---------------------------------------------------------------------
  * Weights of one block (spark_model struct ViTBlock).  FP8 weights are
  * 128x128-block quantised with vit_quant_fp8_block128(block_rows = 128).
  * Precision switch (FlashRT section 4: the first 3 blocks stay bf16): when
@@ -292,6 +316,8 @@ typedef struct vit_encoder_weights {
   const uint16_t* patch_b;    /* [1152] */
   vit_block_weights blocks[VIT_DEPTH];
   vit_merger_weights mergers[VIT_NUM_TAPS]; /* DeepStack after 8, 16, 24; final after 27 */
+  const uint16_t* pos_table;  /* [pos_grid_side^2, 1152] bf16, or NULL (no learned table) */
+  int pos_grid_side;          /* G of pos_table (48), 1..1024; ignored when pos_table is NULL */
 } vit_encoder_weights;
 
 /* ---------------------------------------------------------------------
@@ -311,8 +337,11 @@ int vit_block_forward(const vit_block_weights* w, uint16_t* x_inout, int T,
 
 /* ---------------------------------------------------------------------
  * The whole tower (FlashRT section 3): patch embed (bf16 GEMM, K = 1536,
- * plus an optional precomputed [T, 1152] bf16 position table), 27 blocks,
- * and after blocks 8, 16, 24 and 27 the 2x2 merger MLPs.
+ * plus a position embedding), 27 blocks, and after blocks 8, 16, 24 and 27
+ * the 2x2 merger MLPs.  The position embedding added by the patch-embed
+ * epilogue is either w->pos_table resampled to the grids (as by
+ * vit_pos_embed_interp, into the workspace) or a precomputed [T, 1152]
+ * table pos_embed; giving both is a SHAPE error, giving neither adds none.
  * w: host pointer to the weight table (its members are device pointers).
  * pixels: [T, 1536] fp32.  pos_embed: [T, 1152] bf16 or NULL.
  * grid_hw_dev / grid_hw_host: [num_images, 2] int32 patch grids (rows,

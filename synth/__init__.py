@@ -9,7 +9,8 @@ Every tensor comes from numpy's PCG64 seeded with
 and rounded to bf16 (nearest, ties to even) where the tensor is bf16.
 Distributions follow the workloads described for this tower: activations
 ~N(0, 1), GEMM weights ~N(0, 0.02), biases ~N(0, 0.01), LayerNorm gamma
-1 + N(0, 0.02) and beta ~N(0, 0.01), pixels ~U(-1, 1).
+1 + N(0, 0.02) and beta ~N(0, 0.01), pixels ~U(-1, 1); the learned 48 x 48
+position table ~N(0, 0.02) like the other weights.
 """
 
 from __future__ import annotations
@@ -26,7 +27,7 @@ PATCH_DIM, DEPTH, OUT_HIDDEN, MERGED_DIM = 1536, 27, 4096, 4608
 # Tensor tags (stable integers: changing one changes every derived input).
 TAGS = {
     "x": 1, "q": 2, "k": 3, "v": 4, "a": 5, "w": 6, "bias": 7, "residual": 8,
-    "pixels": 9, "pos_embed": 10,
+    "pixels": 9, "pos_embed": 10, "pos_table": 11,
     "ln1_g": 20, "ln1_b": 21, "qkv_w": 22, "qkv_b": 23, "proj_w": 24, "proj_b": 25,
     "ln2_g": 26, "ln2_b": 27, "fc1_w": 28, "fc1_b": 29, "fc2_w": 30, "fc2_b": 31,
     "patch_w": 40, "patch_b": 41,

@@ -148,6 +148,28 @@ def test_merge_validation_statuses(lib):
     assert f(A, 1152, None, grids, 2, 28, C, D, 1e-6, E, None) == NULL
 
 
+def test_pos_embed_interp_validation(lib):
+    f = lib.vit_pos_embed_interp
+    grids = _cu([46, 136, 3, 5])
+    T = 46 * 136 + 15
+    assert f(A, 48, 1152, B, grids, 2, T + 1, C, 1152, None) == SEQ      # sum h*w != T
+    assert f(A, 48, 1152, B, _cu([0, 5]), 1, 0, C, 1152, None) == SEQ    # empty side
+    assert f(A, 0, 1152, B, grids, 2, T, C, 1152, None) == SHAPE         # G < 1
+    assert f(A, 1025, 1152, B, grids, 2, T, C, 1152, None) == SHAPE
+    assert f(A, 48, 1150, B, grids, 2, T, C, 1152, None) == SHAPE        # dim % 8
+    assert f(A, 48, 1152, B, grids, 2, T, C, 1148, None) == SHAPE        # ld_out < dim
+    assert f(A, 48, 1152, B, grids, 2, T, C, 1156, None) == SHAPE        # ld_out % 8
+    assert f(A, 48, 1152, B, None, 2, T, C, 1152, None) == NULL          # host grids
+    assert f(None, 48, 1152, B, grids, 2, T, C, 1152, None) == NULL
+    assert f(A, 48, 1152, None, grids, 2, T, C, 1152, None) == NULL
+    assert f(A, 48, 1152, B, grids, 2, T, None, 1152, None) == NULL
+    assert f(A + 8, 48, 1152, B, grids, 2, T, C, 1152, None) == ALIGN
+    assert f(A, 48, 1152, B, grids, 2, T, C + 8, 1152, None) == ALIGN
+    assert f(A, 48, 1152, B, grids, 2, T, A + 4096, 1152, None) == ALIAS  # out over the table
+    assert f(A, 48, 1152, B, grids, 2, T, B - 64, 1152, None) == ALIAS    # out over the grids
+    assert f(A, 48, 1152, B, _cu([]), 0, 0, C, 1152, None) == OK          # nothing to do
+
+
 BF16_BLOCK_FIELDS = ("qkv_w", "proj_w", "fc1_w", "fc2_w")
 FP8_MERGER_FIELDS = ("fc1_codes", "fc1_scales", "fc2_codes", "fc2_scales")
 
@@ -236,6 +258,15 @@ def test_encoder_validation(lib):
     assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need, None) == NULL
     w.blocks[13].proj_bias = A
     assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, WSP + 1024, None, WSP, need, None) == ALIAS
+    # learned position table: one position source, a valid side, aligned
+    w.pos_table, w.pos_grid_side = F, 48
+    assert f(ctypes.byref(w), PIX, F + (1 << 24), GD, grids, 1, T, OUT, None, WSP, need, None) == SHAPE
+    w.pos_grid_side = 0
+    assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need, None) == SHAPE
+    w.pos_table, w.pos_grid_side = F + 8, 48
+    assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need, None) == ALIGN
+    w.pos_table = F
+    assert f(ctypes.byref(w), PIX, None, GD, grids, 1, T, OUT, None, WSP, need - 256, None) == WS
 
 
 def test_workspace_sizes_monotone(lib):

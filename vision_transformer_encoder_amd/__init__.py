@@ -35,7 +35,7 @@ _ROOT = os.path.dirname(_PKG)
 library_path = os.path.join(_PKG, "libvit.so")
 header_path = os.path.join(_ROOT, "include", "vit.h")
 
-ABI_VERSION = 3  # VIT_ABI_VERSION of the include/vit.h these signatures follow
+ABI_VERSION = 4  # VIT_ABI_VERSION of the include/vit.h these signatures follow
 HIDDEN, HEADS, HEAD_DIM, MLP, MLP_PADDED = 1152, 16, 72, 4304, 4352
 PATCH_DIM, DEPTH, OUT_HIDDEN, MERGED_DIM, NUM_TAPS = 1536, 27, 4096, 4608, 4
 EPI_BIAS, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_FP8 = 0, 1, 2
@@ -73,7 +73,7 @@ class _MergerW(ctypes.Structure):
 
 class _EncoderW(ctypes.Structure):
     _fields_ = [("patch_w", _P), ("patch_b", _P), ("blocks", _BlockW * DEPTH),
-                ("mergers", _MergerW * NUM_TAPS)]
+                ("mergers", _MergerW * NUM_TAPS), ("pos_table", _P), ("pos_grid_side", _I)]
 
 
 _SIGS = {
@@ -89,6 +89,7 @@ _SIGS = {
     "vit_attention_workspace_size": (_SZ, []),
     "vit_attention": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "vit_merge2x2_layernorm": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, _F, _P, _P]),
+    "vit_pos_embed_interp": (_I, [_P, _I, _I, _P, _P, _I, _I, _P, _I64, _P]),
     "vit_block_workspace_size": (_SZ, [_I]),
     "vit_block_forward": (_I, [ctypes.POINTER(_BlockW), _P, _I, _P, _P, _P, _I, _P, _SZ, _P]),
     "vit_encoder_workspace_size": (_SZ, [_I, _I]),
@@ -314,6 +315,26 @@ def vit_merge2x2_layernorm(x: torch.Tensor, grids: Sequence[Tuple[int, int]], ga
     return out
 
 
+def vit_pos_embed_interp(table: torch.Tensor, grids: Sequence[Tuple[int, int]], grid_side: Optional[int] = None,
+                         grid_dev: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The learned [G*G, D] position table resampled to the grids: [T, D] bf16."""
+    GG, D = table.shape
+    G = int(round(math.sqrt(GG))) if grid_side is None else int(grid_side)
+    g_h, g_ptr = _host_i32(np.asarray(grids, dtype=np.int32).reshape(-1, 2))
+    T = int(sum(int(h) * int(w) for h, w in g_h))
+    if grid_dev is None:
+        grid_dev = torch.from_numpy(g_h.copy()).to(table.device)
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=table.device)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != (T, D) or out.device != table.device
+          or out.stride(1) != 1):
+        raise ValueError(f"output buffer must be a bfloat16 [{T}, {D}] tensor with unit column stride "
+                         "(rows may be strided)")
+    _call("vit_pos_embed_interp", _p(table), G, D, _p(grid_dev), g_ptr, len(g_h), T, _p(out), _row_ld(out),
+          _stream(table.device))
+    return out
+
+
 def vit_block_workspace_size(T: int) -> int:
     return int(require_library().vit_block_workspace_size(T))
 
@@ -382,9 +403,11 @@ class MergerWeights:
 
 class EncoderWeights:
     def __init__(self, patch: dict, blocks: Sequence[dict], mergers: Sequence[dict], device,
-                 bf16_blocks: int = 0, fp8_mergers: bool = False):
+                 bf16_blocks: int = 0, fp8_mergers: bool = False, pos_table=None):
         """bf16_blocks: the first n blocks run in bf16 (FlashRT keeps 3);
-        fp8_mergers: the mergers run their linears in FP8."""
+        fp8_mergers: the mergers run their linears in FP8; pos_table: the
+        learned [G*G, 1152] position table (bf16 bits), resampled to each
+        forward's grids and added after the patch embedding."""
         if len(blocks) != DEPTH or len(mergers) != NUM_TAPS:
             raise ValueError("the tower has 27 blocks and 4 mergers")
         if not 0 <= bf16_blocks <= DEPTH:
@@ -398,6 +421,13 @@ class EncoderWeights:
             s.blocks[i] = b.struct
         for i, m in enumerate(self.mergers):
             s.mergers[i] = m.struct
+        self.pos_table = None
+        if pos_table is not None:
+            self.pos_table = bf16_from_bits(pos_table, device)
+            g = int(round(math.sqrt(self.pos_table.shape[0])))
+            if g * g != self.pos_table.shape[0] or self.pos_table.shape[1] != HIDDEN:
+                raise ValueError("pos_table must be [G*G, 1152]")
+            s.pos_table, s.pos_grid_side = _p(self.pos_table), g
         self.struct = s
 
 

@@ -512,6 +512,31 @@ int vit_block_forward(const vit_block_weights* w, uint16_t* x_inout, int T, cons
                                        static_cast<hipStream_t>(stream)));
 }
 
+int vit_pos_embed_interp(const uint16_t* table, int grid_side, int dim, const int32_t* grid_hw_dev,
+                         const int32_t* grid_hw_host, int num_images, int T, uint16_t* out, int64_t ld_out,
+                         vit_stream_t stream) {
+  if (grid_side < 1 || grid_side > 1024 || dim < 8 || (dim % 8) || dim > kMaxDim || T < 0 || T > kMaxTokens ||
+      num_images < 0 || num_images > (1 << 20) || ld_out < dim || (ld_out & 7))
+    return VIT_ERR_SHAPE;
+  if (num_images > 0 && !grid_hw_host) return VIT_ERR_NULL;
+  int64_t total = 0;
+  for (int j = 0; j < num_images; ++j) {
+    const int h = grid_hw_host[2 * j], w = grid_hw_host[2 * j + 1];
+    if (h < 1 || w < 1 || h > kMaxTokens || w > kMaxTokens) return VIT_ERR_SEQLENS;
+    total += (int64_t)h * w;
+    if (total > T) return VIT_ERR_SEQLENS;
+  }
+  if (total != T) return VIT_ERR_SEQLENS;
+  if (T == 0) return VIT_OK;
+  if (!table || !grid_hw_dev || !out) return VIT_ERR_NULL;
+  if (!al16(table) || !al16(grid_hw_dev) || !al16(out)) return VIT_ERR_ALIGN;
+  const size_t tb = (size_t)grid_side * grid_side * dim * 2;
+  const size_t ob = ((size_t)(T - 1) * ld_out + dim) * 2;
+  if (overlap(out, ob, table, tb) || overlap(out, ob, grid_hw_dev, (size_t)num_images * 8)) return VIT_ERR_ALIAS;
+  return hip_status(vit::launch_pos_interp(table, grid_side, dim, grid_hw_dev, num_images, T, out, ld_out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t vit_encoder_workspace_size(int T, int num_images) {
   if (T < 0 || T > kMaxTokens || num_images < 0 || num_images > (1 << 20)) return 0;
   return encoder_ws_layout(nullptr, T, num_images).bytes;
@@ -533,6 +558,8 @@ int vit_encoder_forward(const vit_encoder_weights* w, const float* pixels, const
     const int st = check_merger_weights(&w->mergers[m]);
     if (st != VIT_OK) return st;
   }
+  if (w->pos_table && (pos_embed || w->pos_grid_side < 1 || w->pos_grid_side > 1024)) return VIT_ERR_SHAPE;
+  if (w->pos_table && !al16(w->pos_table)) return VIT_ERR_ALIGN;
   if (num_images > 0 && !grid_hw_host) return VIT_ERR_NULL;
   if (num_images == 0) return T == 0 ? VIT_OK : VIT_ERR_SEQLENS;
   if (!valid_grids(grid_hw_host, num_images, T)) return VIT_ERR_SEQLENS;
@@ -560,8 +587,17 @@ int vit_encoder_forward(const vit_encoder_weights* w, const float* pixels, const
   uint16_t* x = last_hidden ? last_hidden : ws.x;
   hipError_t e;
   if ((e = vit::launch_geometry(grid_hw_dev, num_images, T, ws.cu, ws.pos, s)) != hipSuccess) return VIT_ERR_HIP;
-  if ((e = vit::launch_bf16_gemm(pixels, true, w->patch_w, T, VIT_HIDDEN, VIT_PATCH_DIM, w->patch_b, pos_embed,
-                                 pos_embed ? VIT_BEPI_BIAS_ADD : VIT_BEPI_BIAS, x, VIT_HIDDEN, s)) != hipSuccess)
+  // the learned table resampled to the grids goes to the qkv region, which
+  // the blocks only use later
+  const uint16_t* pos_add = pos_embed;
+  if (w->pos_table) {
+    if ((e = vit::launch_pos_interp(w->pos_table, w->pos_grid_side, VIT_HIDDEN, grid_hw_dev, num_images, T,
+                                    ws.blk.qkv, VIT_HIDDEN, s)) != hipSuccess)
+      return VIT_ERR_HIP;
+    pos_add = ws.blk.qkv;
+  }
+  if ((e = vit::launch_bf16_gemm(pixels, true, w->patch_w, T, VIT_HIDDEN, VIT_PATCH_DIM, w->patch_b, pos_add,
+                                 pos_add ? VIT_BEPI_BIAS_ADD : VIT_BEPI_BIAS, x, VIT_HIDDEN, s)) != hipSuccess)
     return VIT_ERR_HIP;
   static const int taps[VIT_NUM_TAPS] = {8, 16, 24, 27};
   int ti = 0;

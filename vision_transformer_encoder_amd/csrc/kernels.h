@@ -53,4 +53,7 @@ hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_
 hipError_t launch_geometry(const int32_t* grid_hw, int num_images, int T, int32_t* cu,
                            int32_t* pos, hipStream_t stream);
 
+hipError_t launch_pos_interp(const uint16_t* table, int G, int D, const int32_t* grid_hw, int num_images, int T,
+                             uint16_t* out, int64_t ldo, hipStream_t stream);
+
 }  // namespace vit

@@ -142,4 +142,76 @@ hipError_t launch_geometry(const int32_t* grid_hw, int num_images, int T, int32_
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- position table
+// Learned position embedding resampled to each image's grid (FlashRT page,
+// section 3: "patch_embed -> +interpolated pos_embed"; spark_model page,
+// struct VisionEncoder: a [G*G, 1152] bf16 table, G = num_grid_per_side =
+// 48, with an f32 host copy).  Corner-aligned bilinear samples: token (r, c)
+// of an h x w image reads the table at y = (G-1) r / (h-1), x = (G-1) c /
+// (w-1) (0 for a single row or column), in f32 with every operation rounded
+// in this order and nothing contracted into an FMA:
+//   w00 = (1-dy)(1-dx), w01 = (1-dy) dx, w10 = dy (1-dx), w11 = dy dx,
+//   v = ((w00 T[y0,x0] + w01 T[y0,x1]) + w10 T[y1,x0]) + w11 T[y1,x1],
+// stored as bf16.  One wave per token, 8 features per lane per step; the four
+// table rows of a token are contiguous 16-byte loads.
+__global__ __launch_bounds__(256) void pos_interp_kernel(const uint16_t* __restrict__ table, int G, int D,
+                                                         const int32_t* __restrict__ grid_hw, int num_images,
+                                                         int T, uint16_t* __restrict__ out, int64_t ldo) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int tok0 = 0, h = 1, w = 1;
+  for (int j = 0; j < num_images; ++j) {
+    const int hh = grid_hw[2 * j], ww = grid_hw[2 * j + 1];
+    if (t < tok0 + hh * ww) {
+      h = hh;
+      w = ww;
+      break;
+    }
+    tok0 += hh * ww;
+  }
+  const int local = t - tok0, r = local / w, c = local % w;
+  // (G-1) i is an exact f32 integer; the division is correctly rounded
+  const float y = h > 1 ? ((float)(G - 1) * (float)r) / (float)(h - 1) : 0.0f;
+  const float x = w > 1 ? ((float)(G - 1) * (float)c) / (float)(w - 1) : 0.0f;
+  const int y0 = (int)floorf(y), x0 = (int)floorf(x);
+  const int y1 = min(y0 + 1, G - 1), x1 = min(x0 + 1, G - 1);
+  const float dy = y - (float)y0, dx = x - (float)x0;
+  const float w00 = (1.0f - dy) * (1.0f - dx), w01 = (1.0f - dy) * dx;
+  const float w10 = dy * (1.0f - dx), w11 = dy * dx;
+  const uint16_t* r00 = table + (int64_t)(y0 * G + x0) * D;
+  const uint16_t* r01 = table + (int64_t)(y0 * G + x1) * D;
+  const uint16_t* r10 = table + (int64_t)(y1 * G + x0) * D;
+  const uint16_t* r11 = table + (int64_t)(y1 * G + x1) * D;
+  uint16_t* orow = out + (int64_t)t * ldo;
+  for (int ch = lane; ch < (D >> 3); ch += 64) {
+    float a[8], b[8], e[8], f[8];
+    load8_bf16(r00, ch * 8, D, a);
+    load8_bf16(r01, ch * 8, D, b);
+    load8_bf16(r10, ch * 8, D, e);
+    load8_bf16(r11, ch * 8, D, f);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float s01 = w00 * a[i] + w01 * b[i];
+      const float s2 = s01 + w10 * e[i];
+      v[i] = s2 + w11 * f[i];
+    }
+    uint4 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    o.z = pack_bf16x2(v[4], v[5]);
+    o.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(orow + ch * 8) = o;
+  }
+}
+
+hipError_t launch_pos_interp(const uint16_t* table, int G, int D, const int32_t* grid_hw, int num_images, int T,
+                             uint16_t* out, int64_t ldo, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  pos_interp_kernel<<<(T + 3) / 4, 256, 0, stream>>>(table, G, D, grid_hw, num_images, T, out, ldo);
+  return hipGetLastError();
+}
+
 }  // namespace vit
