@@ -11,6 +11,8 @@ written directly from the definitions on the source pages:
   4 (Correctness) and 5 (Notes & limitations);
 * the spark_model source page "layers/vision_encoder.rs" (struct ViTBlock,
   MergerLayer, VisionEncoder: dimensions, weight list, DeepStack indexes);
+* the same FlashRT doc, sections 1 and 5, for the image / video
+  preprocessing in ``preprocess.py`` (smart_resize, temporal frame pairs);
 * TensorRT-Model-Connect PR #2106 "docs(qwen3_omni): record why FP8 is not
   shipped", section Implementation (FP8 scale = amax / 448).
 
@@ -26,3 +28,4 @@ checked, because neither the weights nor the reference model are available.
 """
 
 from .vit_oracle import *  # noqa: F401,F403
+from . import preprocess  # noqa: F401  (image / video input preparation)
