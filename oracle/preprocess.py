@@ -21,7 +21,7 @@ Readings where the pages are silent (each fixed once):
   clamped at 0, upper neighbour clamped to the last row / column), in f32
   with every operation rounded in a fixed order;
 * normalisation: y = v a_c + b_c with a_c = 1/(255 std_c) and
-  b_c = -mean_c/std_c rounded to f32 (mean and std are inputs);
+  b_c = -mean_c/std_c rounded to f32 (mean and std are f32 inputs);
 * patchify: frames 2g and 2g+1 form temporal group g (a missing last frame
   repeats the one before; a still image is one frame), each group is one
   window of (h'/16) x (w'/16) patches in raster order, and a patch vector is
@@ -89,8 +89,13 @@ def resize_bilinear(frame, out_h: int, out_w: int) -> np.ndarray:
 
 
 def normalize_coefficients(mean: Sequence[float], std: Sequence[float]):
-    a = np.array([1.0 / (255.0 * s) for s in std], dtype=np.float64).astype(np.float32)
-    b = np.array([-m / s for m, s in zip(mean, std)], dtype=np.float64).astype(np.float32)
+    """a_c = 1/(255 std_c), b_c = -mean_c/std_c, rounded to f32, from mean
+    and std taken as f32 values (the precision the per-channel constants
+    are given in)."""
+    m32 = [float(np.float32(m)) for m in mean]
+    s32 = [float(np.float32(s)) for s in std]
+    a = np.array([1.0 / (255.0 * s) for s in s32], dtype=np.float64).astype(np.float32)
+    b = np.array([-m / s for m, s in zip(m32, s32)], dtype=np.float64).astype(np.float32)
     return a, b
 
 
