@@ -459,6 +459,13 @@ def time_kernels(vit, W, T, grids, dev, reps, seq, only=None, eager=False):
         "merger_fc2_bf16": (lambda: vit.vit_bf16_gemm(mh, m["m_fc2_w"], bias=m["m_fc2_b"], out=mo),
                             2 * TM * 4096 * 4608, "F16", 4),
     }
+    # input preparation of the page's image (not part of the timed forward):
+    # 2172 x 724 u8 RGB read once, 6256 x 1536 f32 written
+    frames_u8 = (torch.rand((1, 724, 2172, 3), device=dev) * 255).to(torch.uint8)
+    pre_out = torch.empty((6256, 1536), dtype=torch.float32, device=dev)
+    cases["preprocess"] = (lambda: vit.vit_preprocess_frames(frames_u8, (736, 2176), (0.5, 0.5, 0.5),
+                                                             (0.5, 0.5, 0.5), out=pre_out),
+                           724 * 2172 * 3 + 6256 * 1536 * 4, "B", 0)
     # the learned position table resampled to the grids (only with --pos-table
     # in the forward): the table read once, the [T, 1152] result written
     cases["pos_embed_interp"] = (lambda: vit.vit_pos_embed_interp(ptab, grids, out=pe_out),

@@ -261,6 +261,40 @@ int vit_pos_embed_interp(const uint16_t* table, int grid_side, int dim,
                          vit_stream_t stream);
 
 /* ---------------------------------------------------------------------
+ * Input preparation (FlashRT section 1: image preprocessing runs on the GPU
+ * and max_pixels applies the processor's smart_resize, which rounds to the
+ * patch grid; section 5: each image or video frame group is its own
+ * attention window; spark_model PATCH_DIM doc: a patch is 3 x 2 x 16 x 16).
+ *
+ * vit_smart_resize (host only, no GPU work): the resized (height, width)
+ * for an image, multiples of factor (32 = patch 16 x merge 2): each side
+ * rounded to the nearest multiple (ties to even, at least factor); if the
+ * area exceeds max_pixels (> 0), both sides are scaled by
+ * sqrt(height * width / max_pixels) and floored to multiples; if it is
+ * below min_pixels (> 0), scaled up by sqrt(min_pixels / (height * width))
+ * and ceiled.  The 2172 x 724 image gives 736 x 2176 (6256 patches), and at
+ * max_pixels 1e6 / 5e5 / 2.5e5 gives 3888 / 1824 / 972 patches.
+ * Errors: NULL for missing outputs, SHAPE for sizes < 1 or > 2^20.
+ *
+ * vit_preprocess_frames: frames [num_frames, height, width, 3] u8 RGB on the
+ * device -> pixels [ceil(num_frames/2) * (out_height/16) * (out_width/16),
+ * 1536] f32 on the device, the input of vit_encoder_forward with one grid
+ * (out_height/16, out_width/16) per frame pair.  Bilinear resize with
+ * half-pixel centres, y = v / (255 std_c) - mean_c / std_c, patch rows in
+ * raster order per frame pair, each laid out [channel][frame of the
+ * pair][row][col]; a still image is one frame, and an odd last frame is
+ * paired with itself.  mean_host / std_host: 3 floats on the host (std > 0).
+ * out_height, out_width: multiples of 16 (of 32 for the encoder's 2x2
+ * merge), e.g. from vit_smart_resize.  Errors: SHAPE, NULL, ALIGN (pixels
+ * 16-byte aligned), ALIAS (pixels overlapping the frames).
+ * ------------------------------------------------------------------- */
+int vit_smart_resize(int height, int width, int factor, int64_t min_pixels, int64_t max_pixels,
+                     int* out_height, int* out_width);
+int vit_preprocess_frames(const uint8_t* frames, int num_frames, int height, int width,
+                          int out_height, int out_width, const float* mean_host,
+                          const float* std_host, float* pixels, vit_stream_t stream);
+
+/* ---------------------------------------------------------------------
  * Weights of one block (spark_model struct ViTBlock).  FP8 weights are
  * 128x128-block quantised with vit_quant_fp8_block128(block_rows = 128).
  * Precision switch (FlashRT section 4: the first 3 blocks stay bf16): when

@@ -27,7 +27,7 @@ PATCH_DIM, DEPTH, OUT_HIDDEN, MERGED_DIM = 1536, 27, 4096, 4608
 # Tensor tags (stable integers: changing one changes every derived input).
 TAGS = {
     "x": 1, "q": 2, "k": 3, "v": 4, "a": 5, "w": 6, "bias": 7, "residual": 8,
-    "pixels": 9, "pos_embed": 10, "pos_table": 11,
+    "pixels": 9, "pos_embed": 10, "pos_table": 11, "frames": 12,
     "ln1_g": 20, "ln1_b": 21, "qkv_w": 22, "qkv_b": 23, "proj_w": 24, "proj_b": 25,
     "ln2_g": 26, "ln2_b": 27, "fc1_w": 28, "fc1_b": 29, "fc2_w": 30, "fc2_b": 31,
     "patch_w": 40, "patch_b": 41,
@@ -72,6 +72,19 @@ def normal_bf16(config_id: int, tag: str, index: int, shape, std: float = 1.0,
 def uniform_f32(config_id: int, tag: str, index: int, shape, lo: float, hi: float) -> np.ndarray:
     g = rng(config_id, tag, index)
     return (g.random(size=shape, dtype=np.float32) * np.float32(hi - lo) + np.float32(lo)).astype(np.float32)
+
+
+def frames_u8(config_id: int, index: int, shape) -> np.ndarray:
+    """uint8 RGB frames [F, H, W, 3]: a smooth per-frame gradient plus
+    uniform noise, so resampling sees both structure and texture."""
+    g = rng(config_id, "frames", index)
+    F_, H, W, C = shape
+    yy, xx = np.meshgrid(np.linspace(0, 1, H, dtype=np.float32), np.linspace(0, 1, W, dtype=np.float32),
+                         indexing="ij")
+    base = np.stack([yy, xx, 1 - yy], axis=-1)[None] * np.float32(160)
+    shift = g.uniform(0, 40, size=(F_, 1, 1, C)).astype(np.float32)
+    noise = g.uniform(0, 56, size=shape).astype(np.float32)
+    return np.clip(base + shift + noise, 0, 255).astype(np.uint8)
 
 
 def grids_of(config_id: int) -> List[Tuple[int, int]]:

@@ -170,6 +170,45 @@ def test_pos_embed_interp_validation(lib):
     assert f(A, 48, 1152, B, _cu([]), 0, 0, C, 1152, None) == OK          # nothing to do
 
 
+def test_smart_resize_host_logic_reproduces_the_page_table():
+    # a host-only computation: the library is called directly, no GPU work
+    import json
+    facts = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")))
+    f = facts["smart_resize_rows"]
+    for max_pixels, patches in f["rows"]:
+        h, w = vit.vit_smart_resize(f["image_height"], f["image_width"], max_pixels=max_pixels)
+        assert (h // 16) * (w // 16) == patches and h % 32 == 0 and w % 32 == 0
+
+
+@pytest.mark.parametrize("hw", [(100, 100), (17, 900), (4000, 3000), (31, 33), (48, 48), (80, 80), (724, 2172)])
+@pytest.mark.parametrize("limits", [(0, None), (0, 250000), (200000, None), (3136, 1000000)])
+def test_smart_resize_host_logic_matches_the_oracle(hw, limits):
+    from oracle import preprocess as P
+    assert vit.vit_smart_resize(*hw, min_pixels=limits[0], max_pixels=limits[1]) == \
+        P.smart_resize(*hw, min_pixels=limits[0], max_pixels=limits[1])
+
+
+def test_smart_resize_and_preprocess_validation(lib):
+    h, w = ctypes.c_int(0), ctypes.c_int(0)
+    f = lib.vit_smart_resize
+    assert f(0, 10, 32, 0, 0, ctypes.byref(h), ctypes.byref(w)) == SHAPE
+    assert f(10, 10, 0, 0, 0, ctypes.byref(h), ctypes.byref(w)) == SHAPE
+    assert f(10, 10, 32, 0, 0, None, ctypes.byref(w)) == NULL
+    g = lib.vit_preprocess_frames
+    mean = (ctypes.c_float * 3)(0.5, 0.5, 0.5)
+    std = (ctypes.c_float * 3)(0.5, 0.5, 0.5)
+    bad = (ctypes.c_float * 3)(0.5, 0.0, 0.5)
+    m, s_, b_ = (ctypes.cast(x, ctypes.c_void_p) for x in (mean, std, bad))
+    assert g(A, 1, 724, 2172, 736, 2170, m, s_, B, None) == SHAPE    # out width % 16
+    assert g(A, 0, 724, 2172, 736, 2176, m, s_, B, None) == SHAPE    # no frames
+    assert g(A, 1, 724, 2172, 736, 2176, m, b_, B, None) == SHAPE    # std = 0
+    assert g(A, 1, 724, 2172, 736, 2176, None, s_, B, None) == NULL
+    assert g(None, 1, 724, 2172, 736, 2176, m, s_, B, None) == NULL
+    assert g(A, 1, 724, 2172, 736, 2176, m, s_, None, None) == NULL
+    assert g(A, 1, 724, 2172, 736, 2176, m, s_, B + 4, None) == ALIGN
+    assert g(A, 1, 724, 2172, 736, 2176, m, s_, A + 4096, None) == ALIAS
+
+
 BF16_BLOCK_FIELDS = ("qkv_w", "proj_w", "fc1_w", "fc2_w")
 FP8_MERGER_FIELDS = ("fc1_codes", "fc1_scales", "fc2_codes", "fc2_scales")
 

@@ -90,11 +90,13 @@ def test_normalisation_closed_form():
 
 @pytest.mark.parametrize("F_", [1, 2, 3, 4])
 def test_patch_layout_and_temporal_pairs(F_):
-    # identity resize and a = 1, b = 0: every output value is a raw pixel
+    # identity resize, mean 0 and std 1: every output value is the raw pixel
+    # times f32(1/255), so each output names its source pixel
     g = np.random.default_rng(2)
     h, w = 32, 48
     frames = g.integers(0, 256, (F_, h, w, 3), dtype=np.uint8)
-    px, grids = P.preprocess_frames(frames, h, w, (0.0, 0.0, 0.0), (1 / 255, 1 / 255, 1 / 255))
+    px, grids = P.preprocess_frames(frames, h, w, (0.0, 0.0, 0.0), (1.0, 1.0, 1.0))
+    inv255 = np.float32(1.0 / 255.0)
     G = (F_ + 1) // 2
     gh, gw = h // 16, w // 16
     assert grids == [(gh, gw)] * G and px.shape == (G * gh * gw, 1536)
@@ -108,4 +110,5 @@ def test_patch_layout_and_temporal_pairs(F_):
                         for py in range(0, 16, 5):
                             for pxx in range(0, 16, 3):
                                 col = ((c * 2 + t) * 16 + py) * 16 + pxx
-                                assert px[row, col] == frames[f, pr * 16 + py, pc * 16 + pxx, c]
+                                src = np.float32(frames[f, pr * 16 + py, pc * 16 + pxx, c])
+                                assert px[row, col] == np.float32(src * inv255)

@@ -90,6 +90,8 @@ _SIGS = {
     "vit_attention": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "vit_merge2x2_layernorm": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, _F, _P, _P]),
     "vit_pos_embed_interp": (_I, [_P, _I, _I, _P, _P, _I, _I, _P, _I64, _P]),
+    "vit_smart_resize": (_I, [_I, _I, _I, _I64, _I64, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "vit_preprocess_frames": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "vit_block_workspace_size": (_SZ, [_I]),
     "vit_block_forward": (_I, [ctypes.POINTER(_BlockW), _P, _I, _P, _P, _P, _I, _P, _SZ, _P]),
     "vit_encoder_workspace_size": (_SZ, [_I, _I]),
@@ -333,6 +335,33 @@ def vit_pos_embed_interp(table: torch.Tensor, grids: Sequence[Tuple[int, int]], 
     _call("vit_pos_embed_interp", _p(table), G, D, _p(grid_dev), g_ptr, len(g_h), T, _p(out), _row_ld(out),
           _stream(table.device))
     return out
+
+
+def vit_smart_resize(height: int, width: int, factor: int = 32, min_pixels: int = 0,
+                     max_pixels: Optional[int] = None) -> Tuple[int, int]:
+    """Resized (height, width), multiples of ``factor`` (host computation)."""
+    h, w = _I(0), _I(0)
+    _call("vit_smart_resize", int(height), int(width), int(factor), int(min_pixels or 0), int(max_pixels or 0),
+          ctypes.byref(h), ctypes.byref(w))
+    return h.value, w.value
+
+
+def vit_preprocess_frames(frames: torch.Tensor, out_size: Tuple[int, int], mean: Sequence[float],
+                          std: Sequence[float], out: Optional[torch.Tensor] = None):
+    """[F, H, W, 3] uint8 frames on the device -> (pixels [P, 1536] f32, grids):
+    one grid (out_h/16, out_w/16) per frame pair."""
+    if frames.dtype != torch.uint8 or frames.dim() != 4 or frames.shape[3] != 3 or not frames.is_contiguous():
+        raise ValueError("frames must be a contiguous uint8 [F, H, W, 3] tensor")
+    F_, H, W, _ = frames.shape
+    oh, ow = int(out_size[0]), int(out_size[1])
+    G = (F_ + 1) // 2
+    rows = G * (oh // 16) * (ow // 16)
+    out = _out_like(out, (rows, PATCH_DIM), torch.float32, frames.device)
+    m = (ctypes.c_float * 3)(*[float(v) for v in mean])
+    sd = (ctypes.c_float * 3)(*[float(v) for v in std])
+    _call("vit_preprocess_frames", _p(frames), F_, H, W, oh, ow, ctypes.cast(m, _P), ctypes.cast(sd, _P), _p(out),
+          _stream(frames.device))
+    return out, [(oh // 16, ow // 16)] * G
 
 
 def vit_block_workspace_size(T: int) -> int:

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvit.so")
 
-SOURCES = ["quant.hip", "rope.hip", "attention.hip", "gemm.hip", "merge.hip", "abi.cpp"]
+SOURCES = ["quant.hip", "rope.hip", "attention.hip", "gemm.hip", "merge.hip", "preprocess.hip", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

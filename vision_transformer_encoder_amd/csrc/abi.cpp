@@ -512,6 +512,58 @@ int vit_block_forward(const vit_block_weights* w, uint16_t* x_inout, int T, cons
                                        static_cast<hipStream_t>(stream)));
 }
 
+int vit_smart_resize(int height, int width, int factor, int64_t min_pixels, int64_t max_pixels, int* out_height,
+                     int* out_width) {
+  if (!out_height || !out_width) return VIT_ERR_NULL;
+  constexpr int kMaxSide = 1 << 20;
+  if (height < 1 || width < 1 || height > kMaxSide || width > kMaxSide || factor < 1 || factor > kMaxSide)
+    return VIT_ERR_SHAPE;
+  const double f = factor;
+  // nearest multiple, ties to even (the default rounding mode)
+  int64_t h = std::max<int64_t>(factor, (int64_t)std::nearbyint(height / f) * factor);
+  int64_t w = std::max<int64_t>(factor, (int64_t)std::nearbyint(width / f) * factor);
+  const double area = (double)height * (double)width;
+  if (max_pixels > 0 && h * w > max_pixels) {
+    const double beta = std::sqrt(area / (double)max_pixels);
+    h = std::max<int64_t>(factor, (int64_t)std::floor(height / beta / f) * factor);
+    w = std::max<int64_t>(factor, (int64_t)std::floor(width / beta / f) * factor);
+  } else if (min_pixels > 0 && h * w < min_pixels) {
+    const double beta = std::sqrt((double)min_pixels / area);
+    h = (int64_t)std::ceil(height * beta / f) * factor;
+    w = (int64_t)std::ceil(width * beta / f) * factor;
+  }
+  if (h > kMaxSide || w > kMaxSide) return VIT_ERR_SHAPE;
+  *out_height = (int)h;
+  *out_width = (int)w;
+  return VIT_OK;
+}
+
+int vit_preprocess_frames(const uint8_t* frames, int num_frames, int height, int width, int out_height,
+                          int out_width, const float* mean_host, const float* std_host, float* pixels,
+                          vit_stream_t stream) {
+  constexpr int kMaxSide = 1 << 15;
+  if (num_frames < 1 || num_frames > (1 << 16) || height < 1 || width < 1 || height > kMaxSide ||
+      width > kMaxSide || out_height < 16 || out_width < 16 || out_height > kMaxSide || out_width > kMaxSide ||
+      (out_height % 16) || (out_width % 16))
+    return VIT_ERR_SHAPE;
+  if (!mean_host || !std_host) return VIT_ERR_NULL;
+  float a[3], b[3];
+  for (int c = 0; c < 3; ++c) {
+    const double m = mean_host[c], sd = std_host[c];
+    if (!std::isfinite(m) || !std::isfinite(sd) || !(sd > 0.0)) return VIT_ERR_SHAPE;
+    a[c] = (float)(1.0 / (255.0 * sd));
+    b[c] = (float)(-m / sd);
+  }
+  const int64_t rows = (int64_t)((num_frames + 1) / 2) * (out_height / 16) * (out_width / 16);
+  if (rows > (int64_t)kMaxTokens) return VIT_ERR_SHAPE;
+  if (!frames || !pixels) return VIT_ERR_NULL;
+  if (!al16(pixels)) return VIT_ERR_ALIGN;
+  const size_t fb = (size_t)num_frames * height * width * 3, pb = (size_t)rows * VIT_PATCH_DIM * 4;
+  if (overlap(frames, fb, pixels, pb)) return VIT_ERR_ALIAS;
+  return hip_status(vit::launch_preprocess(frames, num_frames, height, width, out_height, out_width, a, b, pixels,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int vit_pos_embed_interp(const uint16_t* table, int grid_side, int dim, const int32_t* grid_hw_dev,
                          const int32_t* grid_hw_host, int num_images, int T, uint16_t* out, int64_t ld_out,
                          vit_stream_t stream) {

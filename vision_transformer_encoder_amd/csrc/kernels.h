@@ -53,6 +53,9 @@ hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_
 hipError_t launch_geometry(const int32_t* grid_hw, int num_images, int T, int32_t* cu,
                            int32_t* pos, hipStream_t stream);
 
+hipError_t launch_preprocess(const uint8_t* frames, int F, int H, int W, int Ho, int Wo, const float a[3],
+                             const float b[3], float* out, hipStream_t stream);
+
 hipError_t launch_pos_interp(const uint16_t* table, int G, int D, const int32_t* grid_hw, int num_images, int T,
                              uint16_t* out, int64_t ldo, hipStream_t stream);
 
