@@ -47,10 +47,13 @@
 //    fixed for the whole loop (no per-tile address arithmetic), and rows
 //    past the last token read as zero in hardware, so no clamping is needed
 //    (rows of the next window inside the batch are finite and masked).
-//  * Items are ordered head-major and cut into 2 x (workgroups) ranges;
-//    workgroup g runs ranges g and g + G, and ids are mapped so that each
-//    XCD takes a contiguous run: an XCD's 32 workgroups work on one head at
-//    a time, whose K/V then stays in the XCD's L2 (two heads do not fit).
+//  * Items are ordered head-major and cut into one range per workgroup
+//    (a range holds about 1.5 items at 6256 tokens, so at most one cut per
+//    range boundary), with ids mapped so that each XCD takes a contiguous
+//    run of the order: an XCD's 32 workgroups share two heads' K/V in its
+//    L2.  Two rounds of half-size ranges would give each XCD one head at a
+//    time (a third of the L2 misses) but cut nearly every item: the kernel
+//    time is the same and the combine takes half again as long.
 #include <algorithm>
 #include <atomic>
 
@@ -346,9 +349,8 @@ constexpr int kSlotRows = kHD + 2;
 constexpr int kSlotFloats = kSlotRows * kBQ;
 constexpr int kMaxWorkgroups = 256;
 // The work order is cut into rounds x workgroups equal ranges; workgroup g
-// runs ranges g, g + G, ... in turn.  With the XCD-grouped workgroup ids, the
-// workgroups of one XCD then share one head at a time (with 16 heads and 8
-// XCDs, two rounds): one head's K/V fits in the XCD's L2, where two do not.
+// runs ranges g, g + G, ... in turn (one round by default; the partial
+// workspace is sized for up to kMaxRounds).
 constexpr int kMaxRounds = 2;
 constexpr int kMaxRanges = kMaxWorkgroups * kMaxRounds;
 #ifndef VIT_ATTN_ROUNDS
@@ -713,9 +715,8 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   a.num_seqs = num_seqs;
   a.heads = heads;
   a.total = total_tokens;
-  // every range must own at least one key tile; one round per 8 heads (the
-  // XCD count), at most kMaxRounds
-  const int rounds = std::min(kMaxRounds, VIT_ATTN_ROUNDS > 0 ? VIT_ATTN_ROUNDS : std::max(1, heads / 8));
+  // every range must own at least one key tile; one round unless overridden
+  const int rounds = std::min(kMaxRounds, VIT_ATTN_ROUNDS > 0 ? VIT_ATTN_ROUNDS : 1);
   a.num_wgs = (int)std::min<int64_t>(attention_slots(), a.work);
   a.num_ranges = (int)std::min<int64_t>((int64_t)a.num_wgs * rounds, a.work);
   a.scale_log2 = scale * 1.4426950408889634f;
