@@ -446,45 +446,70 @@ __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__
     __syncthreads();
   }
 
-  float* c_lds = reinterpret_cast<float*>(smem);
-  park_acc(c_lds, acc, wn, wm, l32, g);
-  __syncthreads();
+  // epilogue: bias and the added rows are loaded before the tile is parked,
+  // and all eight rows of a thread are read from LDS before the first is
+  // finished (as in the FP8 kernel)
   const int cc = (tid & 15) * 8;
   const int n = n0 + cc;
   float b8[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) b8[j] = (bias && n + j < N) ? bf2f(bias[n + j]) : 0.0f;
   const bool vec = n + 8 <= N && (N & 7) == 0 && (ld_out & 7) == 0;
-#pragma unroll 2
+  uint4 add8[8];
+  if constexpr (EPI == 2) {
+    if (add && vec) {
+#pragma unroll
+      for (int pass = 0; pass < 8; ++pass) {
+        const int m = min(m0 + (tid >> 4) + 16 * pass, M - 1);
+        add8[pass] = *reinterpret_cast<const uint4*>(add + (int64_t)m * N + n);
+      }
+    }
+  }
+  float* c_lds = reinterpret_cast<float*>(smem);
+  park_acc(c_lds, acc, wn, wm, l32, g);
+  tile_barrier();
+  float4 cv[8][2];
+#pragma unroll
   for (int pass = 0; pass < 8; ++pass) {
     const int ml = (tid >> 4) + 16 * pass;
-    const int m = m0 + ml;
-    if (m >= M) continue;
-    const float4 c0 = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc);
-    const float4 c1 = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc + 4);
+    cv[pass][0] = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc);
+    cv[pass][1] = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc + 4);
+  }
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int m = m0 + (tid >> 4) + 16 * pass;
+    const float4 c0 = cv[pass][0], c1 = cv[pass][1];
     float y[8] = {c0.x + b8[0], c0.y + b8[1], c0.z + b8[2], c0.w + b8[3],
                   c1.x + b8[4], c1.y + b8[5], c1.z + b8[6], c1.w + b8[7]};
     if constexpr (EPI == 1) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = gelu_tanh(y[j]);
     }
-    if constexpr (EPI == 2) {
-      if (add) {
+    if (m < M) {
+      if constexpr (EPI == 2) {
+        if (add) {
+          if (vec) {
+            const uint4 u = add8[pass];
+            y[0] += bf_lo(u.x); y[1] += bf_hi(u.x); y[2] += bf_lo(u.y); y[3] += bf_hi(u.y);
+            y[4] += bf_lo(u.z); y[5] += bf_hi(u.z); y[6] += bf_lo(u.w); y[7] += bf_hi(u.w);
+          } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] += (n + j < N) ? bf2f(add[(int64_t)m * N + n + j]) : 0.0f;
+            for (int j = 0; j < 8; ++j) y[j] += (n + j < N) ? bf2f(add[(int64_t)m * N + n + j]) : 0.0f;
+          }
+        }
       }
-    }
-    if (vec) {
-      uint4 o;
-      o.x = pack_bf16x2(y[0], y[1]);
-      o.y = pack_bf16x2(y[2], y[3]);
-      o.z = pack_bf16x2(y[4], y[5]);
-      o.w = pack_bf16x2(y[6], y[7]);
-      *reinterpret_cast<uint4*>(out + (int64_t)m * ld_out + n) = o;
-    } else {
+      if (vec) {
+        uint4 o;
+        o.x = pack_bf16x2(y[0], y[1]);
+        o.y = pack_bf16x2(y[2], y[3]);
+        o.z = pack_bf16x2(y[4], y[5]);
+        o.w = pack_bf16x2(y[6], y[7]);
+        *reinterpret_cast<uint4*>(out + (int64_t)m * ld_out + n) = o;
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (n + j < N) out[(int64_t)m * ld_out + n + j] = f2bf(y[j]);
+        for (int j = 0; j < 8; ++j)
+          if (n + j < N) out[(int64_t)m * ld_out + n + j] = f2bf(y[j]);
+      }
     }
   }
 }

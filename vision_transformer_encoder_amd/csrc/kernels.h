@@ -40,7 +40,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
                             int64_t ld_qkv, uint16_t* o, int64_t ld_o, const int32_t* cu,
                             int num_seqs, int total_tokens, int64_t work_per_head, int heads,
                             float scale, float* partial, hipStream_t stream);
-// Sum over windows of (128-query tiles x 64-key tiles).
+// Sum over windows of (256-query tiles x 64-key tiles).
 int64_t attention_work_per_head(const int32_t* cu_host, int num_seqs);
 size_t attention_partial_bytes();
 
