@@ -39,6 +39,14 @@ __global__ __launch_bounds__(256) void merge_layernorm_kernel(const uint16_t* __
                       tok0 + (2 * R + 1) * w + 2 * C + 1};
   const int D4 = 4 * D;
   const int nchunk = D4 >> 3, cpd = D >> 3;
+  // gamma and beta travel with the row (one memory round trip, not two)
+  uint4 gw[NC], bw[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int ch = min(i * 64 + lane, nchunk - 1);
+    gw[i] = *reinterpret_cast<const uint4*>(gamma + ch * 8);
+    bw[i] = *reinterpret_cast<const uint4*>(beta + ch * 8);
+  }
   float v[NC][8];
   float sum = 0.0f;
 #pragma unroll
@@ -71,9 +79,10 @@ __global__ __launch_bounds__(256) void merge_layernorm_kernel(const uint16_t* __
   for (int i = 0; i < NC; ++i) {
     const int ch = i * 64 + lane;
     if (ch < nchunk) {
-      float gg[8], bb[8];
-      load8_bf16(gamma, ch * 8, D4, gg);
-      load8_bf16(beta, ch * 8, D4, bb);
+      const float gg[8] = {bf_lo(gw[i].x), bf_hi(gw[i].x), bf_lo(gw[i].y), bf_hi(gw[i].y),
+                           bf_lo(gw[i].z), bf_hi(gw[i].z), bf_lo(gw[i].w), bf_hi(gw[i].w)};
+      const float bb[8] = {bf_lo(bw[i].x), bf_hi(bw[i].x), bf_lo(bw[i].y), bf_hi(bw[i].y),
+                           bf_lo(bw[i].z), bf_hi(bw[i].z), bf_lo(bw[i].w), bf_hi(bw[i].w)};
       uint4 o;
       o.x = pack_bf16x2((v[i][0] - mean) * rstd * gg[0] + bb[0], (v[i][1] - mean) * rstd * gg[1] + bb[1]);
       o.y = pack_bf16x2((v[i][2] - mean) * rstd * gg[2] + bb[2], (v[i][3] - mean) * rstd * gg[3] + bb[3]);

@@ -124,6 +124,14 @@ __global__ __launch_bounds__(256) void layernorm_quant_kernel(const uint16_t* __
   if (row >= M) return;
   const int nchunk = D >> 3;
   const uint16_t* xr = x + (int64_t)row * ldx;
+  // gamma and beta travel with the row (one memory round trip, not two)
+  uint4 gw[NC], bw[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int ch = min(i * 64 + lane, nchunk - 1);
+    gw[i] = *reinterpret_cast<const uint4*>(gamma + ch * 8);
+    bw[i] = *reinterpret_cast<const uint4*>(beta + ch * 8);
+  }
   float v[NC][8];
   float sum = 0.0f;
 #pragma unroll
@@ -159,9 +167,10 @@ __global__ __launch_bounds__(256) void layernorm_quant_kernel(const uint16_t* __
     const bool live = ch < nchunk;
     float y[8];
     if (live) {
-      float g[8], bb[8];
-      load8_bf16(gamma, ch * 8, D, g);
-      load8_bf16(beta, ch * 8, D, bb);
+      const float g[8] = {bf_lo(gw[i].x), bf_hi(gw[i].x), bf_lo(gw[i].y), bf_hi(gw[i].y),
+                          bf_lo(gw[i].z), bf_hi(gw[i].z), bf_lo(gw[i].w), bf_hi(gw[i].w)};
+      const float bb[8] = {bf_lo(bw[i].x), bf_hi(bw[i].x), bf_lo(bw[i].y), bf_hi(bw[i].y),
+                           bf_lo(bw[i].z), bf_hi(bw[i].z), bf_lo(bw[i].w), bf_hi(bw[i].w)};
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = (v[i][j] - mean) * rstd * g[j] + bb[j];
     } else {
