@@ -30,13 +30,15 @@
 //  * Software pipeline across key tiles: while the VALU turns S(j) into P(j)
 //    (exp2 with the scale folded in), the MFMA unit already computes S(j+1);
 //    then the PV MFMAs of tile j run, interleaved by hand with the row max
-//    of S(j+1).  K and V^T tiles live in a 4-buffer LDS ring with one
-//    barrier per tile; a tile is stored two steps before its K is read, and
-//    its global loads are issued two steps before that (two register sets).
+//    of S(j+1).  K and V^T tiles live in a 6-buffer LDS ring with one
+//    barrier per two tiles; a tile is stored three steps before its K is
+//    read, and its global loads are issued two steps before that (two
+//    register sets).  Halving the barriers (a 4-buffer ring, one barrier per
+//    tile, is the other build option) takes 2-3 % off the kernel.
 //  * The two waves that share a SIMD run opposite phases: waves 4..7 take
-//    each tile's barrier between their QK/exp phase (VALU-heavy) and their
-//    PV phase (MFMA-heavy), waves 0..3 after the PV phase, so one wave's
-//    exp work overlaps the other's PV MFMAs.
+//    each barrier between their QK/exp phase (VALU-heavy) and their PV phase
+//    (MFMA-heavy), waves 0..3 after the PV phase, so one wave's exp work
+//    overlaps the other's PV MFMAs.
 //  * The running max is only raised (and O rescaled) when a row max grows
 //    by more than 2^8 over it: exact after the final division by the row
 //    sum, and it removes the per-tile rescale of 48 accumulators.
@@ -82,13 +84,21 @@ constexpr int kVBuf = kVRows * kVS;
 // VALU-heavy, one MFMA-heavy) instead of competing for the same unit.
 // 0: no late group; 1: waves 4..7; 2: odd waves.
 constexpr int kSkew = VIT_ATTN_SKEW;
-// A tile is stored kAhead steps before the step whose QK phase reads it, and
-// its stage is reused kStages tiles later.  Between a barrier and the next,
-// the early group runs QK(j) PV(j) and the late group PV(j-1) QK(j): the late
-// group's reads of V(j) fall one barrier interval after the early group's,
-// which the fourth stage covers.
-constexpr int kAhead = 2;
-constexpr int kStages = 4;
+// Key tiles per workgroup barrier (1 or 2).  A tile is stored kAhead steps
+// before the step whose QK phase reads it, and its stage is reused kStages
+// tiles later.  One barrier per tile: between a barrier and the next the
+// early group runs QK(j) PV(j) and the late group PV(j-1) QK(j), so the late
+// group's reads of V(j) fall one interval after the early group's, which the
+// fourth stage covers.  One barrier per two tiles (after the odd steps): an
+// interval reads tiles j-1 .. j+2 and writes tiles j+3, j+4, so a tile must be
+// stored three steps ahead and the ring needs six stages.
+#ifndef VIT_ATTN_SYNC
+#define VIT_ATTN_SYNC 2
+#endif
+constexpr int kSync = VIT_ATTN_SYNC;
+static_assert(kSync == 1 || kSync == 2, "one barrier per one or two key tiles");
+constexpr int kAhead = kSync == 1 ? 2 : 3;
+constexpr int kStages = kSync == 1 ? 4 : 6;
 constexpr float kLazy = 8.0f;     // rescale only when the max grows by > 2^8
 #ifndef VIT_ATTN_FRAG_AHEAD
 #define VIT_ATTN_FRAG_AHEAD 2
@@ -499,7 +509,7 @@ __device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& 
   // tile j+kAhead+2 is fetched into r (past the segment these are harmless
   // extra loads into a free stage).  Then the interleaved MFMA/VALU work of
   // the tile, with this wave group's barrier after its QK or its PV phase.
-  auto body = [&](int j, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2], KVRegs& r) {
+  auto body = [&](int j, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2], KVRegs& r, bool sync) {
     const int bk = next_stage(bv, 1);       // stage of tile j+1
     const int bw = next_stage(bv, kAhead);  // stage for tile j+kAhead
     rescale();
@@ -507,11 +517,11 @@ __device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& 
     mask_last(s.kt + j + kAhead, bw);
     load_kv(r, plan, a.k, a.v, ld, row0 + (j + kAhead + 2) * kBK, a.total, tid);
     auto hook = [&](int slot) {
-      if (kLate && slot == 9) lds_barrier();
+      if (kLate && sync && slot == 9) lds_barrier();
     };
     mx = tile_step(s_nxt, acc, s_cur, ks_mem + bk * kKBuf, vt_mem + bv * kVBuf, qf, scale_log2, m_run, l32, g,
                    vrow2, hook);
-    if (!kLate) lds_barrier();
+    if (!kLate && sync) lds_barrier();
     bv = bk;
   };
   // Last tile: P and PV only.
@@ -526,11 +536,11 @@ __device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& 
   // swapping roles: no copies
   int j = 0;
   for (; j + 2 < ntiles; j += 2) {
-    body(j, s_a, s_b, r_a);
-    body(j + 1, s_b, s_a, r_b);
+    body(j, s_a, s_b, r_a, kSync == 1);
+    body(j + 1, s_b, s_a, r_b, true);
   }
   if (j + 1 < ntiles) {
-    body(j, s_a, s_b, r_a);
+    body(j, s_a, s_b, r_a, kSync == 1);
     tail(s_b);
   } else {
     tail(s_a);
