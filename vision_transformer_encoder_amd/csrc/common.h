@@ -128,12 +128,13 @@ __device__ __forceinline__ void grouped_tile(int lb, int m_tiles, int n_tiles, i
 // 0.5 x (1 + tanh(u)) = x / (1 + e^(-2u)),  u = sqrt(2/pi) (x + 0.044715 x^3):
 // one exp2 and one reciprocal instead of a tanh, and no cancellation in
 // 1 + tanh(u) for negative x (where that form loses most of its relative
-// precision).  e^(-2u) overflows to +inf for very negative x, giving -0.
+// precision).  The exponent -2 log2(e) u is x (c0 + c1 x^2) with
+// c0 = -2 log2(e) sqrt(2/pi) and c1 = 0.044715 c0: one FMA and one multiply.
+// e^(-2u) overflows to +inf for very negative x, giving -0.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float u = k0 * (x + k1 * x * x * x);
-  const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);  // e^(-2u): -2 log2(e) u
+  constexpr float c0 = -2.302208198144325f;
+  constexpr float c1 = -0.1029432395800235f;
+  const float e = __builtin_amdgcn_exp2f(x * fmaf(c1, x * x, c0));
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
