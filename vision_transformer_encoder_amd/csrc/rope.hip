@@ -103,8 +103,12 @@ __device__ __forceinline__ void rope_angles(float (*cs)[HD / 4][2], int e, const
 
 // Coalesced variant: TPB tokens per workgroup, rows staged in dynamic LDS
 // ([token][q|k][heads * HD] bf16).  Needs heads * HD % 8 == 0 and 16-byte
-// aligned rows (checked by the launcher).
-template <int HD>
+// aligned rows (checked by the launcher).  NPT = 16-byte chunks per thread:
+// every thread issues all its loads before the first wait (addresses
+// clamped into the rows, so no load is conditional), then writes them to
+// LDS; the write-back likewise reads all its chunks before storing.  A loop
+// of load / wait / LDS store would cost one memory round trip per chunk.
+template <int HD, int NPT>
 __global__ __launch_bounds__(256) void rope2d_rows_kernel(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
                                                           int64_t ld, const int32_t* __restrict__ pos, int T,
                                                           int heads, int tpb, float log2_theta) {
@@ -116,11 +120,32 @@ __global__ __launch_bounds__(256) void rope2d_rows_kernel(uint16_t* __restrict__
   const int W = heads * HD, nch = W >> 3;
   const int t0 = blockIdx.x * tpb;
   const int total = tpb * 2 * nch;
-  for (int c = threadIdx.x; c < total; c += 256) {
-    const int r = c / nch, ch = c - r * nch;
-    const int t = t0 + (r >> 1);
-    if (t < T) rows[c] = *reinterpret_cast<const uint4*>(((r & 1) ? k : q) + (int64_t)t * ld + ch * 8);
+  // chunk c = tid + 256 i is (row r, column chunk ch) = divmod(c, nch),
+  // stepped per i without a division; chunks past the end take the last one
+  const int tid = threadIdx.x;
+  const int dr = 256 / nch, dch = 256 - dr * nch;
+  const int r0 = tid / nch, ch0 = tid - r0 * nch;
+  uint4 buf[NPT];
+  {
+    int r = r0, ch = ch0;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const bool in = tid + 256 * i < total;
+      const int rr = in ? r : 2 * tpb - 1, cc = in ? ch : nch - 1;
+      const int t = min(t0 + (rr >> 1), T - 1);
+      buf[i] = *reinterpret_cast<const uint4*>(((rr & 1) ? k : q) + (int64_t)t * ld + cc * 8);
+      r += dr;
+      ch += dch;
+      if (ch >= nch) {
+        ch -= nch;
+        ++r;
+      }
+    }
   }
+  // unconditional, so the loads stay ahead of the first wait: a thread past
+  // the end rewrites chunk total - 1 with the value its owner writes
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) rows[min(tid + 256 * i, total - 1)] = buf[i];
   for (int e = threadIdx.x; e < tpb * 2 * Q4; e += 256)
     rope_angles<HD>(cs[e / (2 * Q4)], e % (2 * Q4), pos, t0 + e / (2 * Q4), T, log2_theta);
   __syncthreads();
@@ -163,10 +188,20 @@ __global__ __launch_bounds__(256) void rope2d_rows_kernel(uint16_t* __restrict__
     }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < total; c += 256) {
-    const int r = c / nch, ch = c - r * nch;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) buf[i] = rows[min(tid + 256 * i, total - 1)];
+  int r = r0, ch = ch0;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
     const int t = t0 + (r >> 1);
-    if (t < T) *reinterpret_cast<uint4*>(((r & 1) ? k : q) + (int64_t)t * ld + ch * 8) = rows[c];
+    if (tid + 256 * i < total && t < T)
+      *reinterpret_cast<uint4*>(((r & 1) ? k : q) + (int64_t)t * ld + ch * 8) = buf[i];
+    r += dr;
+    ch += dch;
+    if (ch >= nch) {
+      ch -= nch;
+      ++r;
+    }
   }
 }
 
@@ -181,8 +216,19 @@ static hipError_t launch_rope2d_hd(uint16_t* q, uint16_t* k, int64_t ld, const i
     const int tpb = (size_t)8 * 2 * W * 2 <= 40960 ? 8 : ((size_t)4 * 2 * W * 2 <= 40960 ? 4 : 0);
     if (tpb > 0) {
       const size_t lds = (size_t)tpb * 2 * W * 2;
-      rope2d_rows_kernel<HD><<<(T + tpb - 1) / tpb, 256, lds, stream>>>(q, k, ld, pos, T, heads, tpb, l2t);
-      return hipGetLastError();
+      const int npt = (tpb * 2 * (W / 8) + 255) / 256;  // <= 10: the rows fit in 40 KB
+      const dim3 grid((T + tpb - 1) / tpb);
+#define VIT_ROPE_ROWS(N)                                                                      \
+  case N:                                                                                     \
+    rope2d_rows_kernel<HD, N><<<grid, 256, lds, stream>>>(q, k, ld, pos, T, heads, tpb, l2t); \
+    return hipGetLastError();
+      switch (npt) {
+        VIT_ROPE_ROWS(1) VIT_ROPE_ROWS(2) VIT_ROPE_ROWS(3) VIT_ROPE_ROWS(4) VIT_ROPE_ROWS(5)
+        VIT_ROPE_ROWS(6) VIT_ROPE_ROWS(7) VIT_ROPE_ROWS(8) VIT_ROPE_ROWS(9) VIT_ROPE_ROWS(10)
+        default:
+          break;
+      }
+#undef VIT_ROPE_ROWS
     }
   }
   rope2d_kernel<HD><<<(T + 3) / 4, 256, 0, stream>>>(q, k, ld, pos, T, heads, l2t);
