@@ -47,20 +47,28 @@ __global__ __launch_bounds__(256) void merge_layernorm_kernel(const uint16_t* __
     gw[i] = *reinterpret_cast<const uint4*>(gamma + ch * 8);
     bw[i] = *reinterpret_cast<const uint4*>(beta + ch * 8);
   }
+  // every lane loads a chunk (lanes past the row re-read its last chunk and
+  // zero the values afterwards), so all of a lane's loads are in flight
+  // together: a load under a branch is followed by a full wait at its end
+  uint4 xw[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int ch = min(i * 64 + lane, nchunk - 1);
+    const int slot = ch / cpd, cc = ch - slot * cpd;
+    xw[i] = *reinterpret_cast<const uint4*>(x + (int64_t)src[slot] * D + cc * 8);
+  }
   float v[NC][8];
   float sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const int ch = i * 64 + lane;
-    if (ch < nchunk) {
-      const int slot = ch / cpd, cc = ch % cpd;
-      load8_bf16(x + (int64_t)src[slot] * D, cc * 8, D, v[i]);
-    } else {
+    const bool live = i * 64 + lane < nchunk;
+    const float t[8] = {bf_lo(xw[i].x), bf_hi(xw[i].x), bf_lo(xw[i].y), bf_hi(xw[i].y),
+                        bf_lo(xw[i].z), bf_hi(xw[i].z), bf_lo(xw[i].w), bf_hi(xw[i].w)};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+      v[i][j] = live ? t[j] : 0.0f;
+      sum += v[i][j];
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sum += v[i][j];
   }
   const float mean = wave_sum(sum) / (float)D4;
   float sq = 0.0f;

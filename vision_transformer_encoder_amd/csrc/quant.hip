@@ -14,10 +14,74 @@ namespace vit {
 
 // ---------------------------------------------------------------- per row
 // One wave per row; blocks of 128 columns, four per wave iteration.
+template <int NI>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                          int rows, int cols, int Cp,
                                                          uint8_t* __restrict__ codes,
                                                          float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* xr = x + (int64_t)row * ldx;
+  const int nblk = Cp >> 7;
+  // pass it covers blocks 4 it .. 4 it + 3, 16 lanes each.  With cols % 8 == 0
+  // (rows 16-byte aligned) every pass's chunk is loaded before the first
+  // reduction, addresses clamped into the row and values past it zeroed: a
+  // load under a branch would be followed by a full wait at its end.
+  float v[NI][8];
+  if ((cols & 7) == 0) {
+    uint4 w[NI];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int b = min(4 * it + (lane >> 4), nblk - 1);
+      w[it] = *reinterpret_cast<const uint4*>(xr + min(b * 128 + (lane & 15) * 8, cols - 8));
+    }
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int b = 4 * it + (lane >> 4), c = b * 128 + (lane & 15) * 8;
+      const bool live = b < nblk && c < cols;
+      const float t[8] = {bf_lo(w[it].x), bf_hi(w[it].x), bf_lo(w[it].y), bf_hi(w[it].y),
+                          bf_lo(w[it].z), bf_hi(w[it].z), bf_lo(w[it].w), bf_hi(w[it].w)};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[it][i] = live ? t[i] : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int b = 4 * it + (lane >> 4);
+      if (b < nblk) {
+        load8_bf16(xr, b * 128 + (lane & 15) * 8, cols, v[it]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[it][i] = 0.0f;
+      }
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int b = 4 * it + (lane >> 4);
+    const int c = b * 128 + (lane & 15) * 8;
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[it][i]));
+    am = group16_max(am);
+    float s, inv;
+    block_scale(am, s, inv);
+    if (b < nblk) {
+      uint2 o;
+      o.x = e4m3x4(v[it][0] * inv, v[it][1] * inv, v[it][2] * inv, v[it][3] * inv);
+      o.y = e4m3x4(v[it][4] * inv, v[it][5] * inv, v[it][6] * inv, v[it][7] * inv);
+      *reinterpret_cast<uint2*>(codes + (int64_t)row * Cp + c) = o;
+      if ((lane & 15) == 0) scales[(int64_t)row * nblk + b] = s;
+    }
+  }
+}
+
+// Rows wider than 64 blocks: the same work as a loop of passes.
+__global__ __launch_bounds__(256) void quant_rows_wide_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                              int rows, int cols, int Cp,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -132,19 +196,24 @@ __global__ __launch_bounds__(256) void layernorm_quant_kernel(const uint16_t* __
     gw[i] = *reinterpret_cast<const uint4*>(gamma + ch * 8);
     bw[i] = *reinterpret_cast<const uint4*>(beta + ch * 8);
   }
+  // every lane loads a chunk (lanes past the row re-read its last chunk and
+  // zero the values afterwards), so all of a lane's loads are in flight
+  // together: a load under a branch is followed by a full wait at its end
+  uint4 xw[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) xw[i] = *reinterpret_cast<const uint4*>(xr + min(i * 64 + lane, nchunk - 1) * 8);
   float v[NC][8];
   float sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const int ch = i * 64 + lane;
-    if (ch < nchunk) {
-      load8_bf16(xr, ch * 8, D, v[i]);
-    } else {
+    const bool live = i * 64 + lane < nchunk;
+    const float t[8] = {bf_lo(xw[i].x), bf_hi(xw[i].x), bf_lo(xw[i].y), bf_hi(xw[i].y),
+                        bf_lo(xw[i].z), bf_hi(xw[i].z), bf_lo(xw[i].w), bf_hi(xw[i].w)};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+      v[i][j] = live ? t[j] : 0.0f;
+      sum += v[i][j];
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sum += v[i][j];
   }
   const float mean = wave_sum(sum) / (float)D;
   float sq = 0.0f;
@@ -213,7 +282,20 @@ __global__ __launch_bounds__(256) void layernorm_quant_kernel(const uint16_t* __
 hipError_t launch_quant_rows(const uint16_t* x, int64_t ldx, int rows, int cols, uint8_t* codes,
                              float* scales, hipStream_t stream) {
   const int Cp = (cols + 127) / 128 * 128;
-  quant_rows_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(x, ldx, rows, cols, Cp, codes, scales);
+  const int ni = (Cp / 128 + 3) / 4;  // passes of four 128-column blocks
+  const dim3 grid((rows + 3) / 4);
+#define VIT_QR_CASE(N)                                                                      \
+  case N:                                                                                   \
+    quant_rows_kernel<N><<<grid, 256, 0, stream>>>(x, ldx, rows, cols, Cp, codes, scales); \
+    break;
+  switch (ni) {
+    VIT_QR_CASE(1) VIT_QR_CASE(2) VIT_QR_CASE(3) VIT_QR_CASE(4) VIT_QR_CASE(5) VIT_QR_CASE(6)
+    VIT_QR_CASE(7) VIT_QR_CASE(8) VIT_QR_CASE(9) VIT_QR_CASE(10) VIT_QR_CASE(11) VIT_QR_CASE(12)
+    VIT_QR_CASE(13) VIT_QR_CASE(14) VIT_QR_CASE(15) VIT_QR_CASE(16)
+    default:
+      quant_rows_wide_kernel<<<grid, 256, 0, stream>>>(x, ldx, rows, cols, Cp, codes, scales);
+  }
+#undef VIT_QR_CASE
   return hipGetLastError();
 }
 
