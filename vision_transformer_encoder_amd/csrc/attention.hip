@@ -649,17 +649,38 @@ __global__ __launch_bounds__(2 * kBQ) void attention_combine_kernel(AttnParams a
       return a.partial + (size_t)(gg == g0 ? 2 * gg + 1 : 2 * gg) * kSlotFloats;
     };
     float m = -INFINITY;
-    for (int gg = g0; gg <= lg; ++gg) m = fmaxf(m, slot_of(gg)[(kHD + 1) * kBQ + qi]);
     float o[kHalf];
-#pragma unroll
-    for (int i = 0; i < kHalf; ++i) o[i] = 0.0f;
     float l = 0.0f;
-    for (int gg = g0; gg <= lg; ++gg) {
-      const float* sl = slot_of(gg);
-      const float w = __builtin_amdgcn_exp2f(sl[(kHD + 1) * kBQ + qi] - m);
-      l = fmaf(w, sl[kHD * kBQ + qi], l);
+    if (lg == g0 + 1) {
+      // two segments, the usual cut: every value loaded before the first
+      // wait (a loop with a run-time trip count waits once per iteration);
+      // the same operations in the same order as the loop below
+      const float* s0 = slot_of(g0);
+      const float* s1 = slot_of(lg);
+      float o0[kHalf], o1[kHalf];
+      const float m0 = s0[(kHD + 1) * kBQ + qi], m1 = s1[(kHD + 1) * kBQ + qi];
+      const float l0 = s0[kHD * kBQ + qi], l1 = s1[kHD * kBQ + qi];
 #pragma unroll
-      for (int i = 0; i < kHalf; ++i) o[i] = fmaf(w, sl[(half * kHalf + i) * kBQ + qi], o[i]);
+      for (int i = 0; i < kHalf; ++i) {
+        o0[i] = s0[(half * kHalf + i) * kBQ + qi];
+        o1[i] = s1[(half * kHalf + i) * kBQ + qi];
+      }
+      m = fmaxf(fmaxf(m, m0), m1);
+      const float w0 = __builtin_amdgcn_exp2f(m0 - m), w1 = __builtin_amdgcn_exp2f(m1 - m);
+      l = fmaf(w1, l1, fmaf(w0, l0, 0.0f));
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) o[i] = fmaf(w1, o1[i], fmaf(w0, o0[i], 0.0f));
+    } else {
+      for (int gg = g0; gg <= lg; ++gg) m = fmaxf(m, slot_of(gg)[(kHD + 1) * kBQ + qi]);
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) o[i] = 0.0f;
+      for (int gg = g0; gg <= lg; ++gg) {
+        const float* sl = slot_of(gg);
+        const float w = __builtin_amdgcn_exp2f(sl[(kHD + 1) * kBQ + qi] - m);
+        l = fmaf(w, sl[kHD * kBQ + qi], l);
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) o[i] = fmaf(w, sl[(half * kHalf + i) * kBQ + qi], o[i]);
+      }
     }
     const float inv_l = 1.0f / l;
     uint2* trow = reinterpret_cast<uint2*>(tile + qi * kRowU4) + half * (kHalf / 4);
