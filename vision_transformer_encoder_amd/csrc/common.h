@@ -138,6 +138,12 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// 8 bf16 (one 16-byte load) as fp32.
+__device__ __forceinline__ void unpack8_bf16(uint4 w, float v[8]) {
+  v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+  v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
+}
+
 // Load 8 bf16 starting at column c of a row as fp32; columns >= cols read 0.
 // The full-vector path needs the row 16-byte aligned and c % 8 == 0.
 __device__ __forceinline__ void load8_bf16(const uint16_t* __restrict__ row, int c, int cols, float v[8]) {

@@ -171,6 +171,10 @@ hipError_t launch_geometry(const int32_t* grid_hw, int num_images, int T, int32_
 //   v = ((w00 T[y0,x0] + w01 T[y0,x1]) + w10 T[y1,x0]) + w11 T[y1,x1],
 // stored as bf16.  One wave per token, 8 features per lane per step; the four
 // table rows of a token are contiguous 16-byte loads.
+// NC = 16-byte chunks per lane: all of a lane's loads (four table rows per
+// chunk) are issued before the first wait.  NC = 0: rows wider than 8192,
+// one chunk per loop trip.
+template <int NC>
 __global__ __launch_bounds__(256) void pos_interp_kernel(const uint16_t* __restrict__ table, int G, int D,
                                                          const int32_t* __restrict__ grid_hw, int num_images,
                                                          int T, uint16_t* __restrict__ out, int64_t ldo) {
@@ -202,12 +206,51 @@ __global__ __launch_bounds__(256) void pos_interp_kernel(const uint16_t* __restr
   const uint16_t* r10 = table + (int64_t)(y1 * G + x0) * D;
   const uint16_t* r11 = table + (int64_t)(y1 * G + x1) * D;
   uint16_t* orow = out + (int64_t)t * ldo;
-  for (int ch = lane; ch < (D >> 3); ch += 64) {
+  const int nch = D >> 3;
+  if constexpr (NC == 0) {
+    for (int ch = lane; ch < nch; ch += 64) {
+      float a[8], b[8], e[8], f[8];
+      load8_bf16(r00, ch * 8, D, a);
+      load8_bf16(r01, ch * 8, D, b);
+      load8_bf16(r10, ch * 8, D, e);
+      load8_bf16(r11, ch * 8, D, f);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float s01 = w00 * a[i] + w01 * b[i];
+        const float s2 = s01 + w10 * e[i];
+        v[i] = s2 + w11 * f[i];
+      }
+      uint4 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      o.z = pack_bf16x2(v[4], v[5]);
+      o.w = pack_bf16x2(v[6], v[7]);
+      *reinterpret_cast<uint4*>(orow + ch * 8) = o;
+    }
+    return;
+  }
+  constexpr int kNC = NC > 0 ? NC : 1;
+  uint4 q[kNC][4];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int ch = min(i * 64 + lane, nch - 1);  // lanes past the row re-read its last chunk
+    q[i][0] = *reinterpret_cast<const uint4*>(r00 + ch * 8);
+    q[i][1] = *reinterpret_cast<const uint4*>(r01 + ch * 8);
+    q[i][2] = *reinterpret_cast<const uint4*>(r10 + ch * 8);
+    q[i][3] = *reinterpret_cast<const uint4*>(r11 + ch * 8);
+  }
+  // every chunk is computed and stored, lanes past the row on their clamped
+  // copy (the same value the owning lane writes there): with no branch, the
+  // compiler keeps the loads ahead of the first wait
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int ch = i * 64 + lane;
     float a[8], b[8], e[8], f[8];
-    load8_bf16(r00, ch * 8, D, a);
-    load8_bf16(r01, ch * 8, D, b);
-    load8_bf16(r10, ch * 8, D, e);
-    load8_bf16(r11, ch * 8, D, f);
+    unpack8_bf16(q[i][0], a);
+    unpack8_bf16(q[i][1], b);
+    unpack8_bf16(q[i][2], e);
+    unpack8_bf16(q[i][3], f);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -220,14 +263,25 @@ __global__ __launch_bounds__(256) void pos_interp_kernel(const uint16_t* __restr
     o.y = pack_bf16x2(v[2], v[3]);
     o.z = pack_bf16x2(v[4], v[5]);
     o.w = pack_bf16x2(v[6], v[7]);
-    *reinterpret_cast<uint4*>(orow + ch * 8) = o;
+    *reinterpret_cast<uint4*>(orow + min(ch, nch - 1) * 8) = o;
   }
 }
 
 hipError_t launch_pos_interp(const uint16_t* table, int G, int D, const int32_t* grid_hw, int num_images, int T,
                              uint16_t* out, int64_t ldo, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  pos_interp_kernel<<<(T + 3) / 4, 256, 0, stream>>>(table, G, D, grid_hw, num_images, T, out, ldo);
+  const dim3 grid((T + 3) / 4);
+#define VIT_PI(N)                                                                                  \
+  case N:                                                                                          \
+    pos_interp_kernel<N><<<grid, 256, 0, stream>>>(table, G, D, grid_hw, num_images, T, out, ldo); \
+    break;
+  switch ((D / 8 + 63) / 64) {
+    VIT_PI(1) VIT_PI(2) VIT_PI(3) VIT_PI(4) VIT_PI(5) VIT_PI(6) VIT_PI(7) VIT_PI(8)
+    VIT_PI(9) VIT_PI(10) VIT_PI(11) VIT_PI(12) VIT_PI(13) VIT_PI(14) VIT_PI(15) VIT_PI(16)
+    default:
+      pos_interp_kernel<0><<<grid, 256, 0, stream>>>(table, G, D, grid_hw, num_images, T, out, ldo);
+  }
+#undef VIT_PI
   return hipGetLastError();
 }
 
