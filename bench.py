@@ -143,8 +143,8 @@ def main() -> int:
                          "timing: the driver of the per-kernel counter profiles")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the tower shards by image with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs the tower on one GPU; --gpus {args.gpus} is not supported "
+              "(a packed batch would shard by image across GPUs with no exchange)", file=sys.stderr)
         return 2
 
     import numpy as np
