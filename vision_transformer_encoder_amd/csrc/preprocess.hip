@@ -35,11 +35,18 @@ struct PreParams {
 
 __global__ __launch_bounds__(256) void preprocess_kernel(PreParams p) {
 #pragma clang fp contract(off)
+  // each thread owns columns tid + 256 k of the patch row (k < 6); all 24 of
+  // its source bytes are loaded before the first wait
+  constexpr int kPer = 1536 / 256;
   const int row = blockIdx.x;
   const int g = row / p.per_group, local = row - g * p.per_group;
   const int pr = local / p.gw, pc = local - pr * p.gw;
   float* orow = p.out + (int64_t)row * 1536;
-  for (int col = threadIdx.x; col < 1536; col += 256) {
+  float px4[kPer][4], ly[kPer], lx[kPer];
+  int cch[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int col = threadIdx.x + 256 * k;
     const int c = col >> 9, t = (col >> 8) & 1, py = (col >> 4) & 15, px = col & 15;
     const int f = min(2 * g + t, p.F - 1);
     const int oy = pr * 16 + py, ox = pc * 16 + px;
@@ -51,17 +58,23 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreParams p) {
     // guards the loads
     const int y0 = min((int)floorf(ys), p.H - 1), x0 = min((int)floorf(xs), p.W - 1);
     const int y1 = min(y0 + 1, p.H - 1), x1 = min(x0 + 1, p.W - 1);
-    const float ly = ys - (float)y0, lx = xs - (float)x0;
-    const float hy = 1.0f - ly, hx = 1.0f - lx;
+    ly[k] = ys - (float)y0;
+    lx[k] = xs - (float)x0;
+    cch[k] = c;
     const uint8_t* fr = p.frames + (int64_t)f * p.H * p.W * 3;
-    const float p00 = (float)fr[((int64_t)y0 * p.W + x0) * 3 + c];
-    const float p01 = (float)fr[((int64_t)y0 * p.W + x1) * 3 + c];
-    const float p10 = (float)fr[((int64_t)y1 * p.W + x0) * 3 + c];
-    const float p11 = (float)fr[((int64_t)y1 * p.W + x1) * 3 + c];
-    const float top = hx * p00 + lx * p01;
-    const float bot = hx * p10 + lx * p11;
-    const float v = hy * top + ly * bot;
-    orow[col] = v * p.a[c] + p.b[c];
+    px4[k][0] = (float)fr[((int64_t)y0 * p.W + x0) * 3 + c];
+    px4[k][1] = (float)fr[((int64_t)y0 * p.W + x1) * 3 + c];
+    px4[k][2] = (float)fr[((int64_t)y1 * p.W + x0) * 3 + c];
+    px4[k][3] = (float)fr[((int64_t)y1 * p.W + x1) * 3 + c];
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const float hy = 1.0f - ly[k], hx = 1.0f - lx[k];
+    const float top = hx * px4[k][0] + lx[k] * px4[k][1];
+    const float bot = hx * px4[k][2] + lx[k] * px4[k][3];
+    const float v = hy * top + ly[k] * bot;
+    const int c = cch[k];
+    orow[threadIdx.x + 256 * k] = v * p.a[c] + p.b[c];
   }
 }
 
