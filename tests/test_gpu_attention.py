@@ -48,6 +48,28 @@ def test_rope2d(gpu, grids, ld):
     assert np.all(res[:, 2304:] == 0), "v slice must be untouched"
 
 
+# other head counts and widths take other chunks-per-thread variants of the
+# staged kernel (1, 3 with a partial last pass, 8), with a ragged last group
+# of tokens (T % 8 != 0)
+@pytest.mark.parametrize("heads,hd", [(2, 64), (4, 72), (8, 128)], ids=["2x64", "4x72", "8x128"])
+def test_rope2d_other_shapes(gpu, heads, hd):
+    grids = [(3, 5), (6, 7)]
+    T = sum(h * w for h, w in grids)
+    W = heads * hd
+    q = synth.normal_bf16(1, "q", 7, (T, W))
+    k = synth.normal_bf16(1, "k", 7, (T, W))
+    qk = torch.zeros((T, 2 * W), dtype=torch.bfloat16, device=gpu)
+    qk[:, :W] = dev_bf16(q, gpu)
+    qk[:, W:] = dev_bf16(k, gpu)
+    pos = synth.positions(grids)
+    announce(f"vit_rope2d T={T} heads={heads} head_dim={hd}")
+    vit.vit_rope2d(qk[:, :W], qk[:, W:], torch.from_numpy(pos).to(gpu), num_heads=heads, head_dim=hd)
+    res = host_f64(qk)
+    for name, src, sl in (("q", q, slice(0, W)), ("k", k, slice(W, 2 * W))):
+        ref = O.rope2d(synth.bf16_bits_to_f64(src), pos, num_heads=heads, head_dim=hd)
+        assert_close(res[:, sl], O.bf16(ref), 1e-2, 0.99999, f"rope {name} {heads}x{hd}")
+
+
 def _attention_case(gpu, grids, cfg=1):
     T = sum(h * w for h, w in grids)
     q0, k0, v = _qkv_bits(cfg, T)

@@ -35,6 +35,18 @@ def test_interp_bit_exact(gpu, grids):
     assert np.array_equal(g, ref), f"{int((g != ref).sum())} of {ref.size} values differ"
 
 
+def test_interp_rows_wider_than_8192(gpu):
+    # more than 16 chunks per lane: the one-chunk-per-trip variant
+    G, D = 3, 8200
+    bits = _table(G, D, cfg=6)
+    grids = [(2, 3), (1, 4)]
+    announce(f"vit_pos_embed_interp G={G} D={D} grids={grids}")
+    got = vit.vit_pos_embed_interp(dev_bf16(bits, gpu), grids)
+    ref = O.pos_embed_interp(synth.bf16_bits_to_f64(bits), grids, grid_side=G)
+    g = host_f64(got)
+    assert np.array_equal(g, ref), f"{int((g != ref).sum())} of {ref.size} values differ"
+
+
 def test_interp_other_table_and_strided_output(gpu):
     G, D = 7, 64
     bits = _table(G, D, cfg=5)
