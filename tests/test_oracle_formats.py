@@ -167,3 +167,37 @@ def test_quantize_weight_blocks_independent_library():
             assert s[i, j] == np.float32(amax) / np.float32(448.0)
             ref = torch_e4m3_codes(blk * inv)
             assert np.array_equal(codes[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128], ref)
+
+
+def test_quantize_zero_scale_threshold_boundary():
+    """Blocks whose amax sits just below and just above 2^-116.  Below, the
+    block gets scale 0 and its codes are signed zeros.  Above, scale and
+    inverse are normal, finite fp32 values (2^-116 / 448 > 2^-126, the
+    smallest normal; 448 / 2^-116 < 2^128), the amax element maps to 448 and
+    the half-step error bound holds.  A mistake in the threshold's
+    comparison, its exponent or the zero path fails one side."""
+    t = 2.0 ** -116
+    below, above = O.f32(t * (1 - 2.0 ** -20)), O.f32(t * (1 + 2.0 ** -20))
+    assert below < t < above  # both are fp32 values on either side of 2^-116
+    g = np.random.default_rng(7)
+    x = np.zeros((3, 128))
+    for r, amax in enumerate((below, above, t)):
+        x[r] = O.f32(g.uniform(-1, 1, 128) * amax)
+        x[r, 5] = -amax
+    codes, s = O.quantize_block128(x, 1)
+    # below the threshold: scale 0, every code a zero of the element's sign
+    assert s[0, 0] == 0.0
+    assert np.all((codes[0] & 0x7F) == 0)
+    assert np.array_equal(codes[0] >> 7, np.signbit(x[0]).astype(np.uint8))
+    # at and above it: normal finite scale, amax -> 448 (code 0xFE for -amax)
+    for r in (1, 2):
+        amax = np.abs(x[r]).max()
+        sv = np.float32(s[r, 0])
+        assert np.isfinite(sv) and sv >= np.finfo(np.float32).tiny
+        assert sv == np.float32(np.float32(amax) / np.float32(448.0))
+        inv = np.float32(448.0) / np.float32(amax)
+        assert np.isfinite(inv) and inv < np.finfo(np.float32).max
+        assert codes[r, 5] == 0xFE
+        deq = O.dequantize_block128(codes[r:r + 1], s[r:r + 1], 1)[0]
+        bound = np.maximum(np.abs(x[r]) * 2.0 ** -4, 2.0 ** -10 * s[r, 0]) * (1 + 1e-6)
+        assert np.all(np.abs(x[r] - deq) <= bound)

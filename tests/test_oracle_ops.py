@@ -110,6 +110,39 @@ def test_rope_row_axis_uses_first_half():
     assert np.array_equal(a[:, :36], b[:, :36]) and not np.allclose(a[:, 36:], b[:, 36:])
 
 
+def test_rope_equals_hf_layout_after_fixed_permutation():
+    """The library (transformers) Qwen-VL vision rotary uses another layout:
+    per token the angles [row f_0..f_17, col f_0..f_17] duplicated to 72 and
+    one rotate_half over the whole head, pairs (i, i + 36).  The reading taken
+    here (dims 0..35 rotate by the row, 36..71 by the column, pairs (i, i + 18)
+    inside each half) is that rotation after a fixed per-head permutation of
+    the dims, the same for q and k, so q.k scores agree: a weight-load
+    permutation of the q and k rows of the qkv weight switches layouts."""
+    from transformers.models.qwen3_vl.modeling_qwen3_vl import (Qwen3VLVisionRotaryEmbedding,
+                                                                 apply_rotary_pos_emb_vision)
+    g = np.random.default_rng(6)
+    T = 40
+    pos = _pos(T, g)
+    q = g.standard_normal((T, 16, 72)).astype(np.float32).astype(np.float64)
+    k = g.standard_normal((T, 16, 72)).astype(np.float32).astype(np.float64)
+    ang = Qwen3VLVisionRotaryEmbedding(36)(torch.from_numpy(pos))        # [T, 36]
+    emb = torch.cat([ang, ang], dim=-1)
+    qh, kh = apply_rotary_pos_emb_vision(torch.from_numpy(q), torch.from_numpy(k), emb.cos(), emb.sin())
+    qh, kh = qh.double().numpy(), kh.double().numpy()
+    # HF dim of each dim of this layout: row pair halves, then column pair halves
+    perm = np.concatenate([np.arange(0, 18), np.arange(36, 54), np.arange(18, 36), np.arange(54, 72)])
+    qr = O.rope2d(q[:, :, perm].reshape(T, 1152), pos).reshape(T, 16, 72)
+    kr = O.rope2d(k[:, :, perm].reshape(T, 1152), pos).reshape(T, 16, 72)
+    tol = 1e-4 * np.abs(q).max()  # the library rotates in fp32 (angles up to ~140 rad)
+    assert np.allclose(qr, qh[:, :, perm], atol=tol, rtol=0)
+    assert np.allclose(kr, kh[:, :, perm], atol=tol, rtol=0)
+    s_r = np.einsum("thd,uhd->htu", qr, kr)
+    s_h = np.einsum("thd,uhd->htu", qh, kh)
+    assert np.allclose(s_r, s_h, atol=1e-3, rtol=0)
+    # without the permutation the two layouts genuinely differ
+    assert not np.allclose(O.rope2d(q.reshape(T, 1152), pos).reshape(T, 16, 72), qh, atol=1e-2)
+
+
 # ---------------------------------------------------------------- attention
 
 def test_attention_matches_torch_sdpa_per_window():
