@@ -33,8 +33,8 @@
 //    of S(j+1).  K and V^T tiles live in a 6-buffer LDS ring with one
 //    barrier per two tiles; a tile is stored three steps before its K is
 //    read, and its global loads are issued two steps before that (two
-//    register sets).  Halving the barriers (a 4-buffer ring, one barrier per
-//    tile, is the other build option) takes 2-3 % off the kernel.
+//    register sets).  Half the barriers of a 4-buffer ring with one barrier
+//    per tile: 2-3 % off the kernel.
 //  * The two waves that share a SIMD run opposite phases: waves 4..7 take
 //    each barrier between their QK/exp phase (VALU-heavy) and their PV phase
 //    (MFMA-heavy), waves 0..3 after the PV phase, so one wave's exp work
@@ -75,35 +75,15 @@ constexpr int kVS = 68;           // V^T row stride in LDS (bf16): 64 used
 constexpr int kKBuf = kBK * kKS;  // elements per K buffer
 constexpr int kVRows = kHD + 2;  // V^T rows 0..71, row 72 = ones, row 73 = zeros
 constexpr int kVBuf = kVRows * kVS;
-#ifndef VIT_ATTN_SKEW
-#define VIT_ATTN_SKEW 1
-#endif
-// Wave groups: the "late" group (one wave of each SIMD) takes the barrier of
-// a key tile between its QK/exp phase and its PV phase, the other group after
-// the PV phase.  The two waves that share a SIMD thus run opposite phases (one
-// VALU-heavy, one MFMA-heavy) instead of competing for the same unit.
-// 0: no late group; 1: waves 4..7; 2: odd waves.
-constexpr int kSkew = VIT_ATTN_SKEW;
-// Key tiles per workgroup barrier (1 or 2).  A tile is stored kAhead steps
-// before the step whose QK phase reads it, and its stage is reused kStages
-// tiles later.  One barrier per tile: between a barrier and the next the
-// early group runs QK(j) PV(j) and the late group PV(j-1) QK(j), so the late
-// group's reads of V(j) fall one interval after the early group's, which the
-// fourth stage covers.  One barrier per two tiles (after the odd steps): an
-// interval reads tiles j-1 .. j+2 and writes tiles j+3, j+4, so a tile must be
-// stored three steps ahead and the ring needs six stages.
-#ifndef VIT_ATTN_SYNC
-#define VIT_ATTN_SYNC 2
-#endif
-constexpr int kSync = VIT_ATTN_SYNC;
-static_assert(kSync == 1 || kSync == 2, "one barrier per one or two key tiles");
-constexpr int kAhead = kSync == 1 ? 2 : 3;
-constexpr int kStages = kSync == 1 ? 4 : 6;
+// Key tiles per workgroup barrier: two.  A tile is stored kAhead = 3 steps
+// before the step whose QK phase reads it, and its stage is reused kStages = 6
+// tiles later: between two barriers (after the odd steps) an interval reads
+// tiles j-1 .. j+2 and writes tiles j+3, j+4.  (One barrier per tile with a
+// 4-stage ring was 2-3 % slower.)
+constexpr int kAhead = 3;
+constexpr int kStages = 6;
 constexpr float kLazy = 8.0f;     // rescale only when the max grows by > 2^8
-#ifndef VIT_ATTN_FRAG_AHEAD
-#define VIT_ATTN_FRAG_AHEAD 2
-#endif
-constexpr int kFragAhead = VIT_ATTN_FRAG_AHEAD;  // LDS operand fragments read this many MFMAs ahead
+constexpr int kFragAhead = 2;     // LDS operand fragments read this many MFMAs ahead
 }  // namespace
 
 __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
@@ -162,10 +142,13 @@ __device__ __forceinline__ KVPlan make_plan(int tid, int64_t ld, int64_t hoff) {
   return p;
 }
 
-// Buffer descriptor over rows [row0, total) of a [total, ld] bf16 array.
+// Buffer descriptor over rows [row0, total) of a [total, ld] bf16 array.  Its
+// record count is clamped to 2^31 - 1 bytes: loads reach at most one 64-row
+// tile past row0, so the clamp only matters where the end of the array is
+// far beyond every load (a window of more than 2^31 bytes of rows).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t ld, int row0, int total) {
   const uint16_t* p = base + (int64_t)row0 * ld;
-  const int64_t bytes = (int64_t)(total - row0) * ld * 2;
+  const int64_t bytes = min((int64_t)(total - row0) * ld * 2, (int64_t)0x7fffffff);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, (int)(bytes > 0 ? bytes : 0),
                                            0x00020000);
 }
@@ -358,14 +341,9 @@ constexpr uint32_t kMaskedKey = 0xff7fu;  // bf16 -3.39e38
 constexpr int kSlotRows = kHD + 2;
 constexpr int kSlotFloats = kSlotRows * kBQ;
 constexpr int kMaxWorkgroups = 256;
-// The work order is cut into rounds x workgroups equal ranges; workgroup g
-// runs ranges g, g + G, ... in turn (one round by default; the partial
-// workspace is sized for up to kMaxRounds).
-constexpr int kMaxRounds = 2;
-constexpr int kMaxRanges = kMaxWorkgroups * kMaxRounds;
-#ifndef VIT_ATTN_ROUNDS
-#define VIT_ATTN_ROUNDS 0
-#endif
+// The work order is cut into one range per workgroup; a range can leave at
+// most two partial slots (an item cut at its start, one cut at its end).
+constexpr int kMaxRanges = kMaxWorkgroups;
 
 struct AttnParams {
   const uint16_t* q;
@@ -536,11 +514,11 @@ __device__ __forceinline__ void run_segment(const AttnParams& a, const Segment& 
   // swapping roles: no copies
   int j = 0;
   for (; j + 2 < ntiles; j += 2) {
-    body(j, s_a, s_b, r_a, kSync == 1);
+    body(j, s_a, s_b, r_a, false);
     body(j + 1, s_b, s_a, r_b, true);
   }
   if (j + 1 < ntiles) {
-    body(j, s_a, s_b, r_a, kSync == 1);
+    body(j, s_a, s_b, r_a, false);
     tail(s_b);
   } else {
     tail(s_a);
@@ -597,8 +575,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams a) {
     *reinterpret_cast<uint32_t*>(vt_mem + st * kVBuf + row * kVS + col) = row == 72 ? 0x3f803f80u : 0u;
   }
 
+  // waves 4..7 are the "late" group: one wave of each SIMD takes the barrier
+  // of a key tile between its QK/exp and its PV phase, so the two waves that
+  // share a SIMD run opposite phases (one VALU-heavy, one MFMA-heavy)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool late = kSkew == 1 ? wave >= 4 : kSkew == 2 ? (wave & 1) != 0 : false;
+  const bool late = wave >= 4;
   const int lg = xcd_logical_block(blockIdx.x, a.num_wgs);
   for (int rg = lg; rg < a.num_ranges; rg += a.num_wgs) {
     int64_t p = range_start(a, rg);
@@ -746,10 +727,9 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   a.num_seqs = num_seqs;
   a.heads = heads;
   a.total = total_tokens;
-  // every range must own at least one key tile; one round unless overridden
-  const int rounds = std::min(kMaxRounds, VIT_ATTN_ROUNDS > 0 ? VIT_ATTN_ROUNDS : 1);
+  // every range must own at least one key tile
   a.num_wgs = (int)std::min<int64_t>(attention_slots(), a.work);
-  a.num_ranges = (int)std::min<int64_t>((int64_t)a.num_wgs * rounds, a.work);
+  a.num_ranges = a.num_wgs;
   a.scale_log2 = scale * 1.4426950408889634f;
   attention_kernel<<<a.num_wgs, kThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();

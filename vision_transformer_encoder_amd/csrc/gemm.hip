@@ -96,13 +96,16 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
   const int n0 = n_tile * kBN, m0 = m_tile * kBM;
   const int Kb = Kp >> 7;
 
-  // per-thread load slots: rows lrow + 32i, 16 bytes at lcol
+  // per-thread load slots: rows lrow + 32i, 16 bytes at lcol, as 32-bit
+  // offsets from the tile's first row (< 128 Kp); the tile bases are 64-bit
   const int lrow = tid >> 3, lcol = (tid & 7) * 16;
+  const uint8_t* a_tile = a + (size_t)m0 * Kp;
+  const uint8_t* w_tile = w + (size_t)n0 * Kp;
   uint32_t a_off[4], w_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a_off[i] = (uint32_t)(min(m0 + lrow + 32 * i, M - 1)) * (uint32_t)Kp + lcol;
-    w_off[i] = (uint32_t)(n0 + lrow + 32 * i) * (uint32_t)Kp + lcol;
+    a_off[i] = (uint32_t)(min(m0 + lrow + 32 * i, M - 1) - m0) * (uint32_t)Kp + lcol;
+    w_off[i] = (uint32_t)(lrow + 32 * i) * (uint32_t)Kp + lcol;
   }
   const float* sa_ptr = a_scales + (size_t)min(m0 + (tid & 127), M - 1) * Kb;
   const float* sw_ptr = w_scales + (size_t)n_tile * Kb;
@@ -110,8 +113,8 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
   u32x4_t ra[4], rw[4];
   float rs = 0.0f;
   auto gload = [&](int kb) {
-    const uint8_t* ak = a + kb * kRowB;
-    const uint8_t* wk = w + kb * kRowB;
+    const uint8_t* ak = a_tile + kb * kRowB;
+    const uint8_t* wk = w_tile + kb * kRowB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ra[i] = *reinterpret_cast<const u32x4_t*>(ak + a_off[i]);
@@ -286,14 +289,11 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
   }
 }
 
-// n tiles per group of the tile order (grouped_tile): groups of at most
-// kGroupN tiles, of near-equal size
-#ifndef VIT_GEMM_GROUP
-#define VIT_GEMM_GROUP 12
-#endif
+// n tiles per group of the tile order (grouped_tile): groups of at most 12
+// tiles, of near-equal size
 static int gemm_group_n(int n_tiles) {
-  if (VIT_GEMM_GROUP <= 0) return n_tiles;
-  const int groups = (n_tiles + VIT_GEMM_GROUP - 1) / VIT_GEMM_GROUP;
+  constexpr int kGroupN = 12;
+  const int groups = (n_tiles + kGroupN - 1) / kGroupN;
   return (n_tiles + groups - 1) / groups;
 }
 
@@ -339,8 +339,8 @@ __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__
                                                         const uint16_t* __restrict__ w, int M, int N,
                                                         int K, int n_tiles, int nblocks, int group_n,
                                                         const uint16_t* __restrict__ bias,
-                                                        const uint16_t* __restrict__ add,
-                                                        uint16_t* __restrict__ out, int64_t ld_out) {
+                                                        const uint16_t* add,  // may be out (in-place add)
+                                                        uint16_t* out, int64_t ld_out) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileB];
   uint8_t* a_lds = smem;
   uint8_t* w_lds = smem + 2 * kTileB;
@@ -356,17 +356,20 @@ __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__
 
   // bf16 A / W: chunk = 8 elements (16 B); row = tid/8 + 32i, col = (tid%8)*8
   // fp32 A: chunk = 4 elements (16 B in, 8 B out); row = tid/16 + 16i, col = (tid%16)*4
+  // element offsets from the tile's first row (< 128 K, 32-bit); the tile
+  // bases are 64-bit
   const int wcol = (tid & 7) * 8;
+  const uint16_t* w_tile = w + (size_t)n0 * K;
   uint32_t w_off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w_off[i] = (uint32_t)min(n0 + (tid >> 3) + 32 * i, N - 1) * (uint32_t)K + wcol;
+  for (int i = 0; i < 4; ++i) w_off[i] = (uint32_t)(min(n0 + (tid >> 3) + 32 * i, N - 1) - n0) * (uint32_t)K + wcol;
   constexpr int NA = A_F32 ? 8 : 4;
   const int acol = A_F32 ? (tid & 15) * 4 : (tid & 7) * 8;
   uint32_t a_off[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int row = A_F32 ? (tid >> 4) + 16 * i : (tid >> 3) + 32 * i;
-    a_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + acol;
+    a_off[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + acol;
   }
 
   u32x4_t rw[4];
@@ -374,17 +377,17 @@ __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__
   f32x4_t ra32[8];
   auto gload = [&](int ks) {
     const int k0 = ks * 64;
-    const uint16_t* wk = w + k0;
+    const uint16_t* wk = w_tile + k0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       rw[i] = (k0 + wcol < K) ? *reinterpret_cast<const u32x4_t*>(wk + w_off[i]) : u32x4_t{0, 0, 0, 0};
     if constexpr (A_F32) {
-      const float* ak = reinterpret_cast<const float*>(a_ptr) + k0;
+      const float* ak = reinterpret_cast<const float*>(a_ptr) + (size_t)m0 * K + k0;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         ra32[i] = (k0 + acol < K) ? *reinterpret_cast<const f32x4_t*>(ak + a_off[i]) : f32x4_t{0, 0, 0, 0};
     } else {
-      const uint16_t* ak = reinterpret_cast<const uint16_t*>(a_ptr) + k0;
+      const uint16_t* ak = reinterpret_cast<const uint16_t*>(a_ptr) + (size_t)m0 * K + k0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         ra16[i] = (k0 + acol < K) ? *reinterpret_cast<const u32x4_t*>(ak + a_off[i]) : u32x4_t{0, 0, 0, 0};
