@@ -141,3 +141,56 @@ def test_attention_constant_v_and_deterministic(gpu):
     # softmax weights sum to one: constant V comes back up to rounding
     vv = synth.bf16_bits_to_f64(vrow)
     assert np.allclose(host_f64(o1), np.repeat(vv, T, 0), rtol=1e-2, atol=1e-2)
+
+
+def _peaky_case(gpu, grids, kind):
+    """q, k with scores spanning tens of log2 units and each query's row max
+    in a late key tile of its window.  Per head a random unit direction u is
+    added to every query (weight cq) and to the keys, with a weight that
+    ramps up along the window ("ramp": the max climbs by ~40 log2 units
+    over the window's key tiles) or only on the window's last three keys
+    ("spike": a jump of ~30 log2 units in the last tile).  The generic part
+    of q is scaled by 3 so that scores are peaky everywhere."""
+    T, _, q, k, vf = _attention_case(gpu, grids)
+    g = np.random.default_rng(11)
+    u = g.standard_normal((16, 72))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    cu = synth.cu_seqlens(grids)
+    w = np.zeros(T)
+    for j in range(len(cu) - 1):
+        a, b = int(cu[j]), int(cu[j + 1])
+        if kind == "ramp":
+            w[a:b] = np.arange(b - a) / (b - a)
+        else:
+            w[b - 3:b] = 1.0
+    cq, ck = (16.0, 16.0) if kind == "ramp" else (12.0, 18.0)
+    qh = 3.0 * q.reshape(T, 16, 72) + cq * u[None]
+    kh = k.reshape(T, 16, 72) + ck * w[:, None, None] * u[None]
+    qp, kp = O.bf16(qh.reshape(T, 1152)), O.bf16(kh.reshape(T, 1152))
+    qkv = torch.empty((T, 3456), dtype=torch.bfloat16, device=gpu)
+    qkv[:, :1152] = torch.from_numpy(qp).to(gpu).to(torch.bfloat16)
+    qkv[:, 1152:2304] = torch.from_numpy(kp).to(gpu).to(torch.bfloat16)
+    qkv[:, 2304:] = torch.from_numpy(vf).to(gpu).to(torch.bfloat16)
+    return T, cu, qkv, qp, kp, vf
+
+
+@pytest.mark.parametrize("kind", ["ramp", "spike"])
+@pytest.mark.parametrize("grids", [[(46, 136)], [(18, 54), (36, 108), (24, 76)]], ids=["p6256", "varlen_6684"])
+def test_attention_peaky_logits(gpu, grids, kind):
+    T, cu, qkv, q, k, v = _peaky_case(gpu, grids, kind)
+    # how peaky the scores are (first window, head 0): the spread of a row
+    # in log2 units, how far its first key tile's max lies below the row max
+    # (the running max must climb by more than the 2^8 lazy-rescale margin),
+    # and how many rows have their max in the last tenth of the window
+    a, b = int(cu[0]), int(cu[1])
+    s = (q[a:b, :72] @ k[a:b, :72].T) / math.sqrt(72) * math.log2(math.e)
+    spread = float(np.median(s.max(axis=1) - s.min(axis=1)))
+    climb = float(np.median(s.max(axis=1) - s[:, :64].max(axis=1)))
+    late = float(np.mean(s.argmax(axis=1) >= 0.9 * (b - a)))
+    announce(f"vit_attention peaky ({kind}) T={T}: median row spread {spread:.1f} log2 units, "
+             f"row max {climb:.1f} above the first key tile's, {100 * late:.0f}% of row maxima in the last tenth")
+    assert spread > 20.0 and climb > 16.0 and late > 0.8
+    o = vit.vit_attention(qkv[:, :1152], qkv[:, 1152:2304], qkv[:, 2304:], cu)
+    torch.cuda.synchronize()
+    ref = O.attention(q, k, v, cu)
+    assert_close(host_f64(o), ref, MAX_REL, MIN_COS, f"attention peaky {kind} T={T}")

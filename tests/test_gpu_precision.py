@@ -47,7 +47,8 @@ def test_block_bf16_parity(gpu, cfg, grids):
     ref = O.block_forward_bf16(x0, OI.block_weights(params), synth.positions(grids), synth.cu_seqlens(grids))
     assert_close(got, ref, MAX_REL, MIN_COS, f"bf16 block T={T}")
     # the residual stream carries most of the output: compare the update too
-    assert_close(got - x0, ref - x0, 5e-2, 0.999, f"bf16 block update T={T}")
+    # (no FP8 requantisation here, so it meets the stated tolerance itself)
+    assert_close(got - x0, ref - x0, 2e-2, 0.9995, f"bf16 block update T={T}")
 
 
 def test_fp8_merger_parity(gpu):

@@ -93,3 +93,31 @@ def test_layernorm_quant(gpu, M):
     flips = int((diff > 0).sum())
     announce(f"LN-quant code flips vs fp64 pre-quant: {flips} of {codes.numel()}")
     assert flips <= max(4, codes.numel() // 2000)
+
+
+@pytest.mark.parametrize("block_rows", [1, 128])
+def test_quant_zero_scale_threshold(gpu, block_rows):
+    """Blocks whose amax lies just below 2^-116 (zero scale, signed-zero
+    codes), exactly at it and just above it (normal scale), with bf16
+    inputs: 2^-116 (1 - 2^-8), 2^-116 and 2^-116 (1 + 2^-7)."""
+    t = 2.0 ** -116
+    amaxes = (t * (1 - 2.0 ** -8), t, t * (1 + 2.0 ** -7), 0.0)
+    g = np.random.default_rng(12)
+    rows = 4 if block_rows == 1 else 512
+    x = np.zeros((rows, 256))
+    for i, amax in enumerate(amaxes):
+        # block i: rows i (1 x 128 blocks) or rows 128 i .. 128 i + 127
+        r = slice(i, i + 1) if block_rows == 1 else slice(128 * i, 128 * (i + 1))
+        blk = O.bf16(g.uniform(-1, 1, (x[r].shape[0], 256)) * amax)
+        blk[0, 3] = -amax
+        blk[0, 200] = amax
+        x[r] = blk
+    bits = synth.f32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f64(bits), x)
+    announce(f"vit_quant_fp8_block128 zero-scale threshold, block_rows={block_rows}")
+    codes, scales = vit.vit_quant_fp8_block128(dev_bf16(bits, gpu), block_rows=block_rows)
+    rc, rs = O.quantize_block128(x, block_rows)
+    assert np.array_equal(host_u8(codes), rc)
+    assert np.array_equal(host_f64(scales), rs)
+    s = host_f64(scales)
+    assert np.all(s[0] == 0) and np.all(s[1] > 0) and np.all(s[2] > 0)
