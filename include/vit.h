@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define VIT_ABI_VERSION 4
+#define VIT_ABI_VERSION 5
 
 /* Model dimensions (FlashRT section 3; spark_model struct VisionEncoder). */
 #define VIT_HIDDEN 1152
@@ -148,8 +148,8 @@ int vit_layernorm(const uint16_t* x, int64_t ld_x, const uint16_t* gamma, const 
  *                          [M, Np/128] = block quant of y per row, per 128
  *                          columns; prequant_debug NULL or [M, Np] fp32 y.
  * bias: [N] bf16 or NULL (zero).  Unused output pointers may be NULL.
- * All leading dimensions are the logical widths (packed rows).  M * Kp and
- * Np * Kp must each be below 2^32 (VIT_ERR_SHAPE).  M == 0 is a no-op.
+ * All leading dimensions are the logical widths (packed rows).  M <= 2^24,
+ * N, K <= 2^20 (VIT_ERR_SHAPE).  M == 0 is a no-op.
  * ------------------------------------------------------------------- */
 #define VIT_EPI_BIAS 0
 #define VIT_EPI_BIAS_RESIDUAL 1
@@ -171,7 +171,7 @@ int vit_fp8_block128_gemm(const uint8_t* a, const float* a_scales,
  * as it is loaded: the fp32 pixel buffer of the patch embedding).
  * w: [N, K] bf16; bias: [N] bf16 or NULL; add: [M, N] bf16 (BIAS_ADD only,
  * NULL = no add); out: [M, ld_out] bf16, ld_out >= N.
- * K % 8 == 0; M * K and N * K below 2^32.  M == 0 is a no-op.
+ * K % 8 == 0; M <= 2^24, N, K <= 2^20.  M == 0 is a no-op.
  * ------------------------------------------------------------------- */
 #define VIT_BEPI_BIAS 0
 #define VIT_BEPI_BIAS_GELU 1
@@ -206,12 +206,12 @@ int vit_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* pos_rc, int 
  * cu_seqlens_dev / cu_seqlens_host: the same num_seqs+1 int32 offsets on the
  * device and on the host (the host copy is read for validation and launch
  * sizing only); cu[0] = 0, non-decreasing, cu[num_seqs] = total_tokens.
- * head_dim must be 72 (VIT_ERR_UNSUPPORTED otherwise); ld_qkv, ld_o % 8 == 0;
- * total_tokens * ld_qkv < 2^31.
+ * head_dim must be 72 (VIT_ERR_UNSUPPORTED otherwise); ld_qkv, ld_o % 8 == 0
+ * and <= 2^24; total_tokens <= 2^22.
  * workspace: >= vit_attention_workspace_size() bytes of device memory,
  * 16-byte aligned, not overlapping q, k, v or o (VIT_ERR_WORKSPACE if
  * missing or too small).  It holds fp32 partial results of (window, head,
- * 128-query) items whose key range is split between workgroups; its
+ * 256-query) items whose key range is split between workgroups; its
  * contents on entry do not matter.  Two calls in flight at once (on
  * different streams) need different workspaces.
  * ------------------------------------------------------------------- */
@@ -231,12 +231,20 @@ int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64
  * (2R, 2C), (2R, 2C+1), (2R+1, 2C), (2R+1, 2C+1) (raster order).
  * x: [T, D] bf16 (D % 8 == 0); gamma, beta: [4D]; out: [T/4, 4D] bf16.
  * grid_hw_dev: [num_images, 2] int32 on the device, grid_hw_host the same
- * on the host (validation: h, w even, sum h*w == T).
+ * on the host (validation: h, w even, sum h*w == T).  cu_seqlens_dev:
+ * [num_images + 1] int32 on the device, the token offsets of the images
+ * (0, h0*w0, h0*w0 + h1*w1, ...; the cu_seqlens of the packing), which the
+ * kernel binary-searches for each merged row's image; it must agree with
+ * the grids (device data is not validated; a mismatch gives wrong values,
+ * never an access outside x).
+ * Errors: SHAPE, SEQLENS (grids), NULL, ALIGN (16-byte pointers), ALIAS
+ * (out overlapping x, the grids or cu_seqlens_dev); nothing enqueued.
  * ------------------------------------------------------------------- */
 int vit_merge2x2_layernorm(const uint16_t* x, int D, const int32_t* grid_hw_dev,
-                           const int32_t* grid_hw_host, int num_images, int T,
-                           const uint16_t* gamma, const uint16_t* beta, float eps,
-                           uint16_t* out, vit_stream_t stream);
+                           const int32_t* cu_seqlens_dev, const int32_t* grid_hw_host,
+                           int num_images, int T, const uint16_t* gamma,
+                           const uint16_t* beta, float eps, uint16_t* out,
+                           vit_stream_t stream);
 
 /* ---------------------------------------------------------------------
  * Learned position embedding resampled to each image's patch grid
@@ -251,16 +259,20 @@ int vit_merge2x2_layernorm(const uint16_t* x, int D, const int32_t* grid_hw_dev,
  * stores bf16.
  * table: [G*G, dim] bf16 (1 <= G <= 1024, dim % 8 == 0).  grid_hw_dev /
  * grid_hw_host: [num_images, 2] int32 (h, w >= 1, sum h*w == T), tokens in
- * raster order per image, images packed in order.  out: [T, ld_out] bf16
- * (ld_out >= dim, ld_out % 8 == 0), written in columns [0, dim).
+ * raster order per image, images packed in order.  cu_seqlens_dev:
+ * [num_images + 1] int32 on the device, the images' token offsets, which
+ * the kernel binary-searches for each token's image (it must agree with
+ * the grids; a mismatch gives wrong values, never an access outside the
+ * table or out).  out: [T, ld_out] bf16 (ld_out >= dim, ld_out % 8 == 0),
+ * written in columns [0, dim).
  * Errors: SHAPE for out-of-range sizes, SEQLENS for grids that do not
  * sum to T, NULL / ALIGN (16-byte pointers) / ALIAS (out overlapping the
- * table or the grids); nothing is enqueued on error.
+ * table, the grids or cu_seqlens_dev); nothing is enqueued on error.
  * ------------------------------------------------------------------- */
 int vit_pos_embed_interp(const uint16_t* table, int grid_side, int dim,
-                         const int32_t* grid_hw_dev, const int32_t* grid_hw_host,
-                         int num_images, int T, uint16_t* out, int64_t ld_out,
-                         vit_stream_t stream);
+                         const int32_t* grid_hw_dev, const int32_t* cu_seqlens_dev,
+                         const int32_t* grid_hw_host, int num_images, int T,
+                         uint16_t* out, int64_t ld_out, vit_stream_t stream);
 
 /* ---------------------------------------------------------------------
  * Input preparation (FlashRT section 1: image preprocessing runs on the GPU

@@ -121,6 +121,7 @@ def test_attention_validation(lib):
                  ctypes.c_size_t(wsb if nb is None else nb), None)
 
     assert call(hd=64) == UNSUP
+    assert call(ld=(1 << 24) + 8) == SHAPE       # row stride above 2^24
     assert call(cuh=bad) == SEQ
     assert call(cuh=dec, T=5) == SEQ
     assert call(T=10) == SEQ                      # last offset != total
@@ -141,33 +142,41 @@ def test_merge_validation_statuses(lib):
     f = lib.vit_merge2x2_layernorm
     grids = _cu([4, 6, 2, 2])
     odd = _cu([3, 6, 2, 2])
-    assert f(A, 1152, B, odd, 2, 22, C, D, 1e-6, E, None) == SEQ
-    assert f(A, 1152, B, grids, 2, 27, C, D, 1e-6, E, None) == SEQ    # sum h*w != T
-    assert f(A, 4000, B, grids, 2, 28, C, D, 1e-6, E, None) == SHAPE  # 4D > 8192
-    assert f(A, 1152, B, grids, 2, 28, C, D, 1e-6, A + 64, None) == ALIAS
-    assert f(A, 1152, None, grids, 2, 28, C, D, 1e-6, E, None) == NULL
+    G = F + 4096  # device token offsets
+    assert f(A, 1152, B, G, odd, 2, 22, C, D, 1e-6, E, None) == SEQ
+    assert f(A, 1152, B, G, grids, 2, 27, C, D, 1e-6, E, None) == SEQ    # sum h*w != T
+    assert f(A, 4000, B, G, grids, 2, 28, C, D, 1e-6, E, None) == SHAPE  # 4D > 8192
+    assert f(A, 1152, B, G, grids, 2, 28, C, D, 1e-6, A + 64, None) == ALIAS
+    assert f(A, 1152, B, G, grids, 2, 28, C, D, 1e-6, G - 64, None) == ALIAS  # out over cu_seqlens
+    assert f(A, 1152, None, G, grids, 2, 28, C, D, 1e-6, E, None) == NULL
+    assert f(A, 1152, B, None, grids, 2, 28, C, D, 1e-6, E, None) == NULL     # device offsets
+    assert f(A, 1152, B, G + 4, grids, 2, 28, C, D, 1e-6, E, None) == ALIGN
 
 
 def test_pos_embed_interp_validation(lib):
     f = lib.vit_pos_embed_interp
     grids = _cu([46, 136, 3, 5])
     T = 46 * 136 + 15
-    assert f(A, 48, 1152, B, grids, 2, T + 1, C, 1152, None) == SEQ      # sum h*w != T
-    assert f(A, 48, 1152, B, _cu([0, 5]), 1, 0, C, 1152, None) == SEQ    # empty side
-    assert f(A, 0, 1152, B, grids, 2, T, C, 1152, None) == SHAPE         # G < 1
-    assert f(A, 1025, 1152, B, grids, 2, T, C, 1152, None) == SHAPE
-    assert f(A, 48, 1150, B, grids, 2, T, C, 1152, None) == SHAPE        # dim % 8
-    assert f(A, 48, 1152, B, grids, 2, T, C, 1148, None) == SHAPE        # ld_out < dim
-    assert f(A, 48, 1152, B, grids, 2, T, C, 1156, None) == SHAPE        # ld_out % 8
-    assert f(A, 48, 1152, B, None, 2, T, C, 1152, None) == NULL          # host grids
-    assert f(None, 48, 1152, B, grids, 2, T, C, 1152, None) == NULL
-    assert f(A, 48, 1152, None, grids, 2, T, C, 1152, None) == NULL
-    assert f(A, 48, 1152, B, grids, 2, T, None, 1152, None) == NULL
-    assert f(A + 8, 48, 1152, B, grids, 2, T, C, 1152, None) == ALIGN
-    assert f(A, 48, 1152, B, grids, 2, T, C + 8, 1152, None) == ALIGN
-    assert f(A, 48, 1152, B, grids, 2, T, A + 4096, 1152, None) == ALIAS  # out over the table
-    assert f(A, 48, 1152, B, grids, 2, T, B - 64, 1152, None) == ALIAS    # out over the grids
-    assert f(A, 48, 1152, B, _cu([]), 0, 0, C, 1152, None) == OK          # nothing to do
+    G = F + 4096  # device token offsets
+    assert f(A, 48, 1152, B, G, grids, 2, T + 1, C, 1152, None) == SEQ      # sum h*w != T
+    assert f(A, 48, 1152, B, G, _cu([0, 5]), 1, 0, C, 1152, None) == SEQ    # empty side
+    assert f(A, 0, 1152, B, G, grids, 2, T, C, 1152, None) == SHAPE         # G < 1
+    assert f(A, 1025, 1152, B, G, grids, 2, T, C, 1152, None) == SHAPE
+    assert f(A, 48, 1150, B, G, grids, 2, T, C, 1152, None) == SHAPE        # dim % 8
+    assert f(A, 48, 1152, B, G, grids, 2, T, C, 1148, None) == SHAPE        # ld_out < dim
+    assert f(A, 48, 1152, B, G, grids, 2, T, C, 1156, None) == SHAPE        # ld_out % 8
+    assert f(A, 48, 1152, B, G, None, 2, T, C, 1152, None) == NULL          # host grids
+    assert f(None, 48, 1152, B, G, grids, 2, T, C, 1152, None) == NULL
+    assert f(A, 48, 1152, None, G, grids, 2, T, C, 1152, None) == NULL
+    assert f(A, 48, 1152, B, None, grids, 2, T, C, 1152, None) == NULL      # device offsets
+    assert f(A, 48, 1152, B, G, grids, 2, T, None, 1152, None) == NULL
+    assert f(A + 8, 48, 1152, B, G, grids, 2, T, C, 1152, None) == ALIGN
+    assert f(A, 48, 1152, B, G, grids, 2, T, C + 8, 1152, None) == ALIGN
+    assert f(A, 48, 1152, B, G + 4, grids, 2, T, C, 1152, None) == ALIGN
+    assert f(A, 48, 1152, B, G, grids, 2, T, A + 4096, 1152, None) == ALIAS  # out over the table
+    assert f(A, 48, 1152, B, G, grids, 2, T, B - 64, 1152, None) == ALIAS    # out over the grids
+    assert f(A, 48, 1152, B, G, grids, 2, T, G - 64, 1152, None) == ALIAS    # out over cu_seqlens
+    assert f(A, 48, 1152, B, G, _cu([]), 0, 0, C, 1152, None) == OK          # nothing to do
 
 
 def test_smart_resize_host_logic_reproduces_the_page_table():

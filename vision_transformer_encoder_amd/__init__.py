@@ -35,7 +35,7 @@ _ROOT = os.path.dirname(_PKG)
 library_path = os.path.join(_PKG, "libvit.so")
 header_path = os.path.join(_ROOT, "include", "vit.h")
 
-ABI_VERSION = 4  # VIT_ABI_VERSION of the include/vit.h these signatures follow
+ABI_VERSION = 5  # VIT_ABI_VERSION of the include/vit.h these signatures follow
 HIDDEN, HEADS, HEAD_DIM, MLP, MLP_PADDED = 1152, 16, 72, 4304, 4352
 PATCH_DIM, DEPTH, OUT_HIDDEN, MERGED_DIM, NUM_TAPS = 1536, 27, 4096, 4608, 4
 EPI_BIAS, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_FP8 = 0, 1, 2
@@ -88,8 +88,8 @@ _SIGS = {
     "vit_rope2d": (_I, [_P, _P, _I64, _P, _I, _I, _I, _F, _P]),
     "vit_attention_workspace_size": (_SZ, []),
     "vit_attention": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _P, _SZ, _P]),
-    "vit_merge2x2_layernorm": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, _F, _P, _P]),
-    "vit_pos_embed_interp": (_I, [_P, _I, _I, _P, _P, _I, _I, _P, _I64, _P]),
+    "vit_merge2x2_layernorm": (_I, [_P, _I, _P, _P, _P, _I, _I, _P, _P, _F, _P, _P]),
+    "vit_pos_embed_interp": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _I64, _P]),
     "vit_smart_resize": (_I, [_I, _I, _I, _I64, _I64, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "vit_preprocess_frames": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "vit_block_workspace_size": (_SZ, [_I]),
@@ -304,36 +304,46 @@ def vit_attention_workspace_size() -> int:
     return int(require_library().vit_attention_workspace_size())
 
 
-def vit_merge2x2_layernorm(x: torch.Tensor, grids: Sequence[Tuple[int, int]], gamma: torch.Tensor,
-                           beta: torch.Tensor, eps: float = 1e-6,
-                           grid_dev: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    T, D = x.shape
+def _grid_arrays(grids, device, grid_dev=None, cu_dev=None):
+    """Host grids [n, 2] int32 (and their address), and the device grids and
+    token offsets cu [n + 1] (uploaded unless given)."""
     g_h, g_ptr = _host_i32(np.asarray(grids, dtype=np.int32).reshape(-1, 2))
     if grid_dev is None:
-        grid_dev = torch.from_numpy(g_h.copy()).to(x.device)
+        grid_dev = torch.from_numpy(g_h.copy()).to(device)
+    if cu_dev is None:
+        cu = np.concatenate([[0], np.cumsum(g_h[:, 0].astype(np.int64) * g_h[:, 1])]).astype(np.int32)
+        cu_dev = torch.from_numpy(cu).to(device)
+    return g_h, g_ptr, grid_dev, cu_dev
+
+
+def vit_merge2x2_layernorm(x: torch.Tensor, grids: Sequence[Tuple[int, int]], gamma: torch.Tensor,
+                           beta: torch.Tensor, eps: float = 1e-6,
+                           grid_dev: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                           cu_dev: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, D = x.shape
+    g_h, g_ptr, grid_dev, cu_dev = _grid_arrays(grids, x.device, grid_dev, cu_dev)
     out = _out_like(out, (T // 4, 4 * D), torch.bfloat16, x.device)
-    _call("vit_merge2x2_layernorm", _p(x), D, _p(grid_dev), g_ptr, len(g_h), T, _p(gamma), _p(beta), eps,
-          _p(out), _stream(x.device))
+    _call("vit_merge2x2_layernorm", _p(x), D, _p(grid_dev), _p(cu_dev), g_ptr, len(g_h), T, _p(gamma), _p(beta),
+          eps, _p(out), _stream(x.device))
     return out
 
 
 def vit_pos_embed_interp(table: torch.Tensor, grids: Sequence[Tuple[int, int]], grid_side: Optional[int] = None,
-                         grid_dev: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         grid_dev: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                         cu_dev: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The learned [G*G, D] position table resampled to the grids: [T, D] bf16."""
     GG, D = table.shape
     G = int(round(math.sqrt(GG))) if grid_side is None else int(grid_side)
-    g_h, g_ptr = _host_i32(np.asarray(grids, dtype=np.int32).reshape(-1, 2))
+    g_h, g_ptr, grid_dev, cu_dev = _grid_arrays(grids, table.device, grid_dev, cu_dev)
     T = int(sum(int(h) * int(w) for h, w in g_h))
-    if grid_dev is None:
-        grid_dev = torch.from_numpy(g_h.copy()).to(table.device)
     if out is None:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=table.device)
     elif (out.dtype != torch.bfloat16 or tuple(out.shape) != (T, D) or out.device != table.device
           or out.stride(1) != 1):
         raise ValueError(f"output buffer must be a bfloat16 [{T}, {D}] tensor with unit column stride "
                          "(rows may be strided)")
-    _call("vit_pos_embed_interp", _p(table), G, D, _p(grid_dev), g_ptr, len(g_h), T, _p(out), _row_ld(out),
-          _stream(table.device))
+    _call("vit_pos_embed_interp", _p(table), G, D, _p(grid_dev), _p(cu_dev), g_ptr, len(g_h), T, _p(out),
+          _row_ld(out), _stream(table.device))
     return out
 
 

@@ -173,7 +173,7 @@ int check_merger_weights(const vit_merger_weights* m, bool* fp8 = nullptr) {
 // of the FP8 activation and hidden codes (unused here), the GELU output
 // [T, 4304] bf16 in the qkv + o regions, dead once proj has read o.
 hipError_t block_forward_bf16_impl(const vit_block_weights* w, uint16_t* x, int T, const int32_t* pos,
-                                   const int32_t* cu_dev, int num_seqs, int64_t attn_work, const BlockWs& ws,
+                                   const int32_t* cu_dev, int num_seqs, const vit::AttnPlan& plan, const BlockWs& ws,
                                    hipStream_t s) {
   constexpr int H = VIT_HIDDEN;
   const size_t t = (size_t)T;
@@ -190,7 +190,7 @@ hipError_t block_forward_bf16_impl(const vit_block_weights* w, uint16_t* x, int 
                                  3 * H, s)) != hipSuccess) return e;
   if ((e = vit::launch_rope2d(ws.qkv, ws.qkv + H, 3 * H, pos, T, VIT_HEADS, VIT_HEAD_DIM, 10000.0f, s)) !=
       hipSuccess) return e;
-  if ((e = launch_attention(ws.qkv, ws.qkv + H, ws.qkv + 2 * H, 3 * H, ws.o, H, cu_dev, num_seqs, T, attn_work,
+  if ((e = launch_attention(ws.qkv, ws.qkv + H, ws.qkv + 2 * H, 3 * H, ws.o, H, cu_dev, num_seqs, T, plan,
                             VIT_HEADS, 1.0f / std::sqrt((float)VIT_HEAD_DIM), ws.attn_part, s)) != hipSuccess)
     return e;
   // x = bf16(x + o W_proj^T + b), in place (each element read before it is written)
@@ -204,10 +204,10 @@ hipError_t block_forward_bf16_impl(const vit_block_weights* w, uint16_t* x, int 
 }
 
 hipError_t block_forward_impl(const vit_block_weights* w, uint16_t* x, int T, const int32_t* pos,
-                              const int32_t* cu_dev, int num_seqs, int64_t attn_work, const BlockWs& ws,
+                              const int32_t* cu_dev, int num_seqs, const vit::AttnPlan& plan, const BlockWs& ws,
                               hipStream_t s) {
   constexpr int H = VIT_HIDDEN;
-  if (w->qkv_w) return block_forward_bf16_impl(w, x, T, pos, cu_dev, num_seqs, attn_work, ws, s);
+  if (w->qkv_w) return block_forward_bf16_impl(w, x, T, pos, cu_dev, num_seqs, plan, ws, s);
   hipError_t e;
   // LN1 -> FP8 (per token, per 128 columns)
   if ((e = vit::launch_layernorm_quant(x, H, w->ln1_gamma, w->ln1_beta, 1e-6f, T, H, ws.a_codes,
@@ -220,7 +220,7 @@ hipError_t block_forward_impl(const vit_block_weights* w, uint16_t* x, int T, co
   if ((e = vit::launch_rope2d(ws.qkv, ws.qkv + H, 3 * H, pos, T, VIT_HEADS, VIT_HEAD_DIM, 10000.0f, s)) !=
       hipSuccess) return e;
   // attention
-  if ((e = launch_attention(ws.qkv, ws.qkv + H, ws.qkv + 2 * H, 3 * H, ws.o, H, cu_dev, num_seqs, T, attn_work,
+  if ((e = launch_attention(ws.qkv, ws.qkv + H, ws.qkv + 2 * H, 3 * H, ws.o, H, cu_dev, num_seqs, T, plan,
                             VIT_HEADS, 1.0f / std::sqrt((float)VIT_HEAD_DIM), ws.attn_part, s)) != hipSuccess)
     return e;
   // proj: x = bf16(x + Q(o) W^T + b)
@@ -239,10 +239,11 @@ hipError_t block_forward_impl(const vit_block_weights* w, uint16_t* x, int T, co
 }
 
 hipError_t merger_forward_impl(const vit_merger_weights* m, const uint16_t* x, const int32_t* grid_dev,
-                               int n, int T, uint16_t* out, const EncoderWs& ws, hipStream_t s) {
+                               const int32_t* cu_dev, int n, int T, uint16_t* out, const EncoderWs& ws,
+                               hipStream_t s) {
   hipError_t e;
   const int TM = T / 4;
-  if ((e = vit::launch_merge_layernorm(x, VIT_HIDDEN, grid_dev, n, T, m->ln_gamma, m->ln_beta, 1e-6f,
+  if ((e = vit::launch_merge_layernorm(x, VIT_HIDDEN, grid_dev, cu_dev, n, T, m->ln_gamma, m->ln_beta, 1e-6f,
                                        ws.m_ln, s)) != hipSuccess) return e;
   if (m->fc1_codes) {
     // "merger FP8" (FlashRT section 1): the block recipe on the 4608-wide
@@ -362,8 +363,8 @@ int vit_fp8_block128_gemm(const uint8_t* a, const float* a_scales, const uint8_t
   const void* all[] = {a, a_scales, w, w_scales, bias, residual, out, out_codes, out_scales, prequant_debug};
   for (const void* p : all)
     if (p && !al16(p)) return VIT_ERR_ALIGN;
+  // operand offsets are 32-bit only inside a 128-row tile (< 128 * Kp)
   const int Kp = ceil128(K), Np = ceil128(N);
-  if ((uint64_t)M * Kp >= ((uint64_t)1 << 32) || (uint64_t)Np * Kp >= ((uint64_t)1 << 32)) return VIT_ERR_SHAPE;
   const size_t ab = (size_t)M * Kp, asb = (size_t)M * (Kp / 128) * 4, wb = (size_t)Np * Kp,
                wsb = (size_t)(Np / 128) * (Kp / 128) * 4, bb = bias ? (size_t)N * 2 : 0;
   const size_t rb = (size_t)M * N * 2;
@@ -394,7 +395,6 @@ int vit_bf16_gemm(const void* a, int a_is_f32, const uint16_t* w, int M, int N, 
   if (M < 0 || N < 1 || K < 8 || (K % 8) || M > kMaxTokens * 4 || N > kMaxDim || K > kMaxDim || ld_out < N)
     return VIT_ERR_SHAPE;
   if (epilogue < VIT_BEPI_BIAS || epilogue > VIT_BEPI_BIAS_ADD) return VIT_ERR_UNSUPPORTED;
-  if ((uint64_t)M * K >= ((uint64_t)1 << 32) || (uint64_t)N * K >= ((uint64_t)1 << 32)) return VIT_ERR_SHAPE;
   if (M == 0) return VIT_OK;
   if (!a || !w || !out) return VIT_ERR_NULL;
   const void* all[] = {a, w, bias, add, out};
@@ -434,16 +434,21 @@ int vit_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* pos_rc, int 
 
 size_t vit_attention_workspace_size(void) { return vit::attention_partial_bytes(); }
 
-int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv, uint16_t* o,
-                  int64_t ld_o, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
-                  int total_tokens, int num_heads, int head_dim, float softmax_scale, void* workspace,
-                  size_t workspace_bytes, vit_stream_t stream) {
+}  // extern "C"
+
+namespace {
+// Validation of an attention call, everything but the workspace.  VIT_OK
+// with *nothing = true: nothing to enqueue.
+int check_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv, const uint16_t* o,
+                    int64_t ld_o, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                    int total_tokens, int num_heads, int head_dim, float softmax_scale, bool* nothing) {
+  *nothing = true;
   if (num_seqs < 0 || num_seqs > (1 << 20) || total_tokens < 0 || total_tokens > kMaxTokens || num_heads < 1 ||
       num_heads > 256)
     return VIT_ERR_SHAPE;
   if (head_dim != VIT_HEAD_DIM) return VIT_ERR_UNSUPPORTED;
   const int64_t width = (int64_t)num_heads * head_dim;
-  if (ld_qkv < width || ld_o < width) return VIT_ERR_SHAPE;
+  if (ld_qkv < width || ld_o < width || ld_qkv > (1 << 24) || ld_o > (1 << 24)) return VIT_ERR_SHAPE;
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return VIT_ERR_SHAPE;
   if (!cu_seqlens_host) return VIT_ERR_NULL;
   if (num_seqs == 0) return total_tokens == 0 ? VIT_OK : VIT_ERR_SEQLENS;
@@ -452,36 +457,58 @@ int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64
   if (!q || !k || !v || !o || !cu_seqlens_dev) return VIT_ERR_NULL;
   if (!al16(q) || !al16(k) || !al16(v) || !al16(o) || !al16(cu_seqlens_dev) || (ld_qkv & 7) || (ld_o & 7))
     return VIT_ERR_ALIGN;
-  if ((int64_t)total_tokens * ld_qkv >= ((int64_t)1 << 31)) return VIT_ERR_SHAPE;
   const size_t ib = ((size_t)(total_tokens - 1) * ld_qkv + width) * 2;
   const size_t ob = ((size_t)(total_tokens - 1) * ld_o + width) * 2;
   if (overlap(o, ob, q, ib) || overlap(o, ob, k, ib) || overlap(o, ob, v, ib)) return VIT_ERR_ALIAS;
+  *nothing = false;
+  return VIT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv, uint16_t* o,
+                  int64_t ld_o, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                  int total_tokens, int num_heads, int head_dim, float softmax_scale, void* workspace,
+                  size_t workspace_bytes, vit_stream_t stream) {
+  bool nothing = true;
+  const int st = check_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                 total_tokens, num_heads, head_dim, softmax_scale, &nothing);
+  if (st != VIT_OK || nothing) return st;
+  const int64_t width = (int64_t)num_heads * head_dim;
+  const size_t ib = ((size_t)(total_tokens - 1) * ld_qkv + width) * 2;
+  const size_t ob = ((size_t)(total_tokens - 1) * ld_o + width) * 2;
   const size_t wb = vit::attention_partial_bytes();
   if (!workspace || workspace_bytes < wb) return VIT_ERR_WORKSPACE;
   if (!al16(workspace)) return VIT_ERR_ALIGN;
   if (overlap(workspace, wb, q, ib) || overlap(workspace, wb, k, ib) || overlap(workspace, wb, v, ib) ||
       overlap(workspace, wb, o, ob))
     return VIT_ERR_ALIAS;
-  const int64_t work = vit::attention_work_per_head(cu_seqlens_host, num_seqs);
-  return hip_status(launch_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, num_seqs, total_tokens, work,
+  vit::AttnPlan plan;
+  vit::plan_attention(cu_seqlens_host, num_seqs, num_heads, &plan);
+  return hip_status(launch_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, num_seqs, total_tokens, plan,
                                      num_heads, softmax_scale, static_cast<float*>(workspace),
                                      static_cast<hipStream_t>(stream)));
 }
 
-int vit_merge2x2_layernorm(const uint16_t* x, int D, const int32_t* grid_hw_dev, const int32_t* grid_hw_host,
-                           int num_images, int T, const uint16_t* gamma, const uint16_t* beta, float eps,
-                           uint16_t* out, vit_stream_t stream) {
+int vit_merge2x2_layernorm(const uint16_t* x, int D, const int32_t* grid_hw_dev, const int32_t* cu_seqlens_dev,
+                           const int32_t* grid_hw_host, int num_images, int T, const uint16_t* gamma,
+                           const uint16_t* beta, float eps, uint16_t* out, vit_stream_t stream) {
   if (D < 8 || (D % 8) || 4 * D > 8192 || T < 0 || T > kMaxTokens || num_images < 0 || num_images > (1 << 20))
     return VIT_ERR_SHAPE;
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return VIT_ERR_SHAPE;
   if (num_images > 0 && !grid_hw_host) return VIT_ERR_NULL;
   if (num_images == 0) return T == 0 ? VIT_OK : VIT_ERR_SEQLENS;
   if (!valid_grids(grid_hw_host, num_images, T)) return VIT_ERR_SEQLENS;
-  if (!x || !grid_hw_dev || !gamma || !beta || !out) return VIT_ERR_NULL;
-  if (!al16(x) || !al16(grid_hw_dev) || !al16(gamma) || !al16(beta) || !al16(out)) return VIT_ERR_ALIGN;
-  if (overlap(out, (size_t)T * D * 2, x, (size_t)T * D * 2)) return VIT_ERR_ALIAS;
-  return hip_status(vit::launch_merge_layernorm(x, D, grid_hw_dev, num_images, T, gamma, beta, eps, out,
-                                                static_cast<hipStream_t>(stream)));
+  if (!x || !grid_hw_dev || !cu_seqlens_dev || !gamma || !beta || !out) return VIT_ERR_NULL;
+  if (!al16(x) || !al16(grid_hw_dev) || !al16(cu_seqlens_dev) || !al16(gamma) || !al16(beta) || !al16(out))
+    return VIT_ERR_ALIGN;
+  const size_t ob = (size_t)T * D * 2;
+  if (overlap(out, ob, x, ob) || overlap(out, ob, grid_hw_dev, (size_t)num_images * 8) ||
+      overlap(out, ob, cu_seqlens_dev, (size_t)(num_images + 1) * 4))
+    return VIT_ERR_ALIAS;
+  return hip_status(vit::launch_merge_layernorm(x, D, grid_hw_dev, cu_seqlens_dev, num_images, T, gamma, beta, eps,
+                                                out, static_cast<hipStream_t>(stream)));
 }
 
 size_t vit_block_workspace_size(int T) {
@@ -507,8 +534,9 @@ int vit_block_forward(const vit_block_weights* w, uint16_t* x_inout, int T, cons
   if (overlap(workspace, ws.bytes, x_inout, (size_t)T * VIT_HIDDEN * 2) ||
       overlap(workspace, ws.bytes, pos_rc, (size_t)T * 8))
     return VIT_ERR_ALIAS;
-  const int64_t work = vit::attention_work_per_head(cu_seqlens_host, num_seqs);
-  return hip_status(block_forward_impl(w, x_inout, T, pos_rc, cu_seqlens_dev, num_seqs, work, ws,
+  vit::AttnPlan plan;
+  vit::plan_attention(cu_seqlens_host, num_seqs, VIT_HEADS, &plan);
+  return hip_status(block_forward_impl(w, x_inout, T, pos_rc, cu_seqlens_dev, num_seqs, plan, ws,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -565,8 +593,8 @@ int vit_preprocess_frames(const uint8_t* frames, int num_frames, int height, int
 }
 
 int vit_pos_embed_interp(const uint16_t* table, int grid_side, int dim, const int32_t* grid_hw_dev,
-                         const int32_t* grid_hw_host, int num_images, int T, uint16_t* out, int64_t ld_out,
-                         vit_stream_t stream) {
+                         const int32_t* cu_seqlens_dev, const int32_t* grid_hw_host, int num_images, int T,
+                         uint16_t* out, int64_t ld_out, vit_stream_t stream) {
   if (grid_side < 1 || grid_side > 1024 || dim < 8 || (dim % 8) || dim > kMaxDim || T < 0 || T > kMaxTokens ||
       num_images < 0 || num_images > (1 << 20) || ld_out < dim || (ld_out & 7))
     return VIT_ERR_SHAPE;
@@ -580,13 +608,15 @@ int vit_pos_embed_interp(const uint16_t* table, int grid_side, int dim, const in
   }
   if (total != T) return VIT_ERR_SEQLENS;
   if (T == 0) return VIT_OK;
-  if (!table || !grid_hw_dev || !out) return VIT_ERR_NULL;
-  if (!al16(table) || !al16(grid_hw_dev) || !al16(out)) return VIT_ERR_ALIGN;
+  if (!table || !grid_hw_dev || !cu_seqlens_dev || !out) return VIT_ERR_NULL;
+  if (!al16(table) || !al16(grid_hw_dev) || !al16(cu_seqlens_dev) || !al16(out)) return VIT_ERR_ALIGN;
   const size_t tb = (size_t)grid_side * grid_side * dim * 2;
   const size_t ob = ((size_t)(T - 1) * ld_out + dim) * 2;
-  if (overlap(out, ob, table, tb) || overlap(out, ob, grid_hw_dev, (size_t)num_images * 8)) return VIT_ERR_ALIAS;
-  return hip_status(vit::launch_pos_interp(table, grid_side, dim, grid_hw_dev, num_images, T, out, ld_out,
-                                           static_cast<hipStream_t>(stream)));
+  if (overlap(out, ob, table, tb) || overlap(out, ob, grid_hw_dev, (size_t)num_images * 8) ||
+      overlap(out, ob, cu_seqlens_dev, (size_t)(num_images + 1) * 4))
+    return VIT_ERR_ALIAS;
+  return hip_status(vit::launch_pos_interp(table, grid_side, dim, grid_hw_dev, cu_seqlens_dev, num_images, T, out,
+                                           ld_out, static_cast<hipStream_t>(stream)));
 }
 
 size_t vit_encoder_workspace_size(int T, int num_images) {
@@ -630,10 +660,12 @@ int vit_encoder_forward(const vit_encoder_weights* w, const float* pixels, const
       overlap(last_hidden, last_hidden ? xb : 0, pos_embed, pos_embed ? xb : 0))
     return VIT_ERR_ALIAS;
 
-  // attention work of the packing, from the host copy of the grids
+  // attention plan of the packing (the same for every block), from the host
+  // copy of the grids
   std::vector<int32_t> cu_host(num_images + 1, 0);
   for (int j = 0; j < num_images; ++j) cu_host[j + 1] = cu_host[j] + grid_hw_host[2 * j] * grid_hw_host[2 * j + 1];
-  const int64_t work = vit::attention_work_per_head(cu_host.data(), num_images);
+  vit::AttnPlan plan;
+  vit::plan_attention(cu_host.data(), num_images, VIT_HEADS, &plan);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint16_t* x = last_hidden ? last_hidden : ws.x;
@@ -643,7 +675,7 @@ int vit_encoder_forward(const vit_encoder_weights* w, const float* pixels, const
   // the blocks only use later
   const uint16_t* pos_add = pos_embed;
   if (w->pos_table) {
-    if ((e = vit::launch_pos_interp(w->pos_table, w->pos_grid_side, VIT_HIDDEN, grid_hw_dev, num_images, T,
+    if ((e = vit::launch_pos_interp(w->pos_table, w->pos_grid_side, VIT_HIDDEN, grid_hw_dev, ws.cu, num_images, T,
                                     ws.blk.qkv, VIT_HIDDEN, s)) != hipSuccess)
       return VIT_ERR_HIP;
     pos_add = ws.blk.qkv;
@@ -655,11 +687,11 @@ int vit_encoder_forward(const vit_encoder_weights* w, const float* pixels, const
   int ti = 0;
   const size_t tap_elems = (size_t)(T / 4) * VIT_OUT_HIDDEN;
   for (int b = 0; b < VIT_DEPTH; ++b) {
-    if ((e = block_forward_impl(&w->blocks[b], x, T, ws.pos, ws.cu, num_images, work, ws.blk, s)) != hipSuccess)
+    if ((e = block_forward_impl(&w->blocks[b], x, T, ws.pos, ws.cu, num_images, plan, ws.blk, s)) != hipSuccess)
       return VIT_ERR_HIP;
     if (ti < VIT_NUM_TAPS && b + 1 == taps[ti]) {
-      if ((e = merger_forward_impl(&w->mergers[ti], x, grid_hw_dev, num_images, T, out + ti * tap_elems, ws, s)) !=
-          hipSuccess)
+      if ((e = merger_forward_impl(&w->mergers[ti], x, grid_hw_dev, ws.cu, num_images, T, out + ti * tap_elems, ws,
+                                   s)) != hipSuccess)
         return VIT_ERR_HIP;
       ++ti;
     }

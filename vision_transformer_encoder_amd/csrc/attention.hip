@@ -340,7 +340,7 @@ constexpr uint32_t kMaskedKey = 0xff7fu;  // bf16 -3.39e38
 // running max m (log2 units), one column per query of the 256-query tile, fp32.
 constexpr int kSlotRows = kHD + 2;
 constexpr int kSlotFloats = kSlotRows * kBQ;
-constexpr int kMaxWorkgroups = 256;
+constexpr int kMaxWorkgroups = kAttnMaxRanges;
 // The work order is cut into one range per workgroup; a range can leave at
 // most two partial slots (an item cut at its start, one cut at its end).
 constexpr int kMaxRanges = kMaxWorkgroups;
@@ -357,39 +357,56 @@ struct AttnParams {
   int64_t work;           // work_per_head * heads
   int num_seqs, heads, total, num_wgs, num_ranges;
   float scale_log2;
+  AttnRangeStart start[kAttnMaxRanges];  // where each range starts (host plan)
 };
 
 // Work item = (head, window, q tile); its key tiles are the unit of work.
 // Items are ordered head-major, so the contiguous ranges that the XCD
 // mapping gives each XCD touch one or two heads' K/V.
 struct Segment {
-  int head, seq_begin, seq_len, qtile, kt, nk;  // kt: first key tile of the segment
+  int head, win, seq_begin, seq_len, qtile, kt, nq, nk;  // kt: first key tile of the segment
 };
 
 __device__ __forceinline__ int64_t range_start(const AttnParams& a, int r) {
   return (int64_t)r * a.work / a.num_ranges;
 }
 
-// Item and key tile at position p of the work order (p < work).
-__device__ Segment locate(const AttnParams& a, int64_t p) {
-  Segment s{};
-  s.head = (int)(p / a.work_per_head);
-  int64_t r = p - (int64_t)s.head * a.work_per_head;
-  for (int w = 0; w < a.num_seqs; ++w) {
-    const int b = a.cu[w], len = a.cu[w + 1] - b;
-    const int nq = (len + kBQ - 1) / kBQ, nk = (len + kBK - 1) / kBK;
-    const int64_t span = (int64_t)nq * nk;
-    if (r < span) {
-      s.seq_begin = b;
-      s.seq_len = len;
-      s.qtile = (int)(r / nk);
-      s.kt = (int)(r % nk);
-      s.nk = nk;
-      break;
-    }
-    r -= span;
-  }
+// Key tile `rem` (q tile rem / nk, key tile rem % nk) of window `win`, head `head`.
+__device__ __forceinline__ Segment segment_at(const AttnParams& a, int head, int win, int rem) {
+  Segment s;
+  s.head = head;
+  s.win = win;
+  s.seq_begin = a.cu[win];
+  s.seq_len = a.cu[win + 1] - s.seq_begin;
+  s.nq = (s.seq_len + kBQ - 1) / kBQ;
+  s.nk = (s.seq_len + kBK - 1) / kBK;
+  s.qtile = rem / max(s.nk, 1);
+  s.kt = rem - s.qtile * s.nk;
   return s;
+}
+
+// First segment of range r: its window and position come from the host's
+// plan, its head from the range's start in the work order.
+__device__ __forceinline__ Segment range_first(const AttnParams& a, int r) {
+  const int head = (int)(range_start(a, r) / a.work_per_head);
+  return segment_at(a, head, a.start[r].win, a.start[r].rem);
+}
+
+// The item after the one s belongs to (its first key tile): the next q tile
+// of the window, else the next non-empty window, else window 0 of the next
+// head.  Only called while work remains, so a non-empty window follows.
+__device__ __forceinline__ Segment next_item(const AttnParams& a, const Segment& s) {
+  if (s.qtile + 1 < s.nq) return segment_at(a, s.head, s.win, (s.qtile + 1) * s.nk);
+  int head = s.head, w = s.win + 1;
+  for (;;) {
+    if (w >= a.num_seqs) {
+      w = 0;
+      ++head;
+    }
+    if (a.cu[w + 1] > a.cu[w]) break;
+    ++w;
+  }
+  return segment_at(a, head, w, 0);
 }
 
 // Key tiles [s.kt, kt_end) of one item: the pipelined flash loop.  With
@@ -584,9 +601,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams a) {
   for (int rg = lg; rg < a.num_ranges; rg += a.num_wgs) {
     int64_t p = range_start(a, rg);
     const int64_t end = range_start(a, rg + 1);
+    Segment s = range_first(a, rg);
     while (p < end) {
-      const Segment s = locate(a, p);
-      if (s.nk == 0) break;  // only if the device windows disagree with the host's work count
+      if (s.nk == 0) break;  // only if the device windows disagree with the host's copy
       const int kt_end = (int)min((int64_t)s.nk, s.kt + (end - p));
       // a segment that starts inside its item uses slot 2 rg, one that starts
       // the item but stops short of its end slot 2 rg + 1
@@ -598,6 +615,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams a) {
       else
         run_segment<false>(a, s, kt_end, slot, ks_mem, vt_mem);
       p += kt_end - s.kt;
+      if (p < end) s = next_item(a, s);  // the segment ran to its item's end
     }
   }
 }
@@ -616,7 +634,7 @@ __global__ __launch_bounds__(2 * kBQ) void attention_combine_kernel(AttnParams a
   const int lg = blockIdx.x;  // range
   const int64_t p = range_start(a, lg), end = range_start(a, lg + 1);
   if (p >= end) return;
-  const Segment s = locate(a, p);
+  const Segment s = range_first(a, lg);
   if (s.nk == 0 || s.kt == 0 || s.kt + (end - p) < s.nk) return;  // not an item's last segment
   const int64_t p0 = p - s.kt;                        // the item's first key tile
   int g0 = (int)(p0 * a.num_ranges / a.work);
@@ -681,15 +699,6 @@ __global__ __launch_bounds__(2 * kBQ) void attention_combine_kernel(AttnParams a
   }
 }
 
-int64_t attention_work_per_head(const int32_t* cu_host, int num_seqs) {
-  int64_t n = 0;
-  for (int s = 0; s < num_seqs; ++s) {
-    const int64_t len = cu_host[s + 1] - cu_host[s];
-    n += ((len + kBQ - 1) / kBQ) * ((len + kBK - 1) / kBK);
-  }
-  return n;
-}
-
 size_t attention_partial_bytes() { return (size_t)2 * kMaxRanges * kSlotFloats * sizeof(float); }
 
 // Resident slots of the current device: one 512-thread workgroup per CU,
@@ -709,10 +718,50 @@ static int attention_slots() {
   return slots;
 }
 
+// Host plan of the stream-K split.  The work order of one head lists, per
+// window, its q tiles x key tiles; the whole order is heads x that list,
+// cut into one equal range per workgroup.  For each range the window and
+// the position inside that window's list where it starts are found in one
+// sweep over the windows (the ranges visited in order of their in-head
+// position), so the kernels locate every segment in constant time.
+void plan_attention(const int32_t* cu_host, int num_seqs, int heads, AttnPlan* plan) {
+  int64_t wph = 0;
+  for (int w = 0; w < num_seqs; ++w) {
+    const int64_t len = cu_host[w + 1] - cu_host[w];
+    wph += ((len + kBQ - 1) / kBQ) * ((len + kBK - 1) / kBK);
+  }
+  plan->work_per_head = wph;
+  plan->num_ranges = 0;
+  if (wph == 0) return;
+  const int64_t work = wph * heads;
+  const int R = (int)std::min<int64_t>(attention_slots(), work);
+  plan->num_ranges = R;
+  int64_t rel[kAttnMaxRanges];
+  int order[kAttnMaxRanges];
+  for (int r = 0; r < R; ++r) {
+    const int64_t p = (int64_t)r * work / R;
+    rel[r] = p - (p / wph) * wph;
+    order[r] = r;
+  }
+  std::sort(order, order + R, [&](int x, int y) { return rel[x] < rel[y]; });
+  int64_t acc = 0;
+  int i = 0;
+  for (int w = 0; w < num_seqs && i < R; ++w) {
+    const int64_t len = cu_host[w + 1] - cu_host[w];
+    const int64_t span = ((len + kBQ - 1) / kBQ) * ((len + kBK - 1) / kBK);
+    while (i < R && rel[order[i]] < acc + span) {
+      plan->start[order[i]].win = w;
+      plan->start[order[i]].rem = (int32_t)(rel[order[i]] - acc);
+      ++i;
+    }
+    acc += span;
+  }
+}
+
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv, uint16_t* o,
-                            int64_t ld_o, const int32_t* cu, int num_seqs, int total_tokens, int64_t work_per_head,
+                            int64_t ld_o, const int32_t* cu, int num_seqs, int total_tokens, const AttnPlan& plan,
                             int heads, float scale, float* partial, hipStream_t stream) {
-  if (work_per_head == 0) return hipSuccess;
+  if (plan.work_per_head == 0) return hipSuccess;
   AttnParams a;
   a.q = q;
   a.k = k;
@@ -722,15 +771,15 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   a.partial = partial;
   a.ld = ld_qkv;
   a.ldo = ld_o;
-  a.work_per_head = work_per_head;
-  a.work = work_per_head * heads;
+  a.work_per_head = plan.work_per_head;
+  a.work = plan.work_per_head * heads;
   a.num_seqs = num_seqs;
   a.heads = heads;
   a.total = total_tokens;
-  // every range must own at least one key tile
-  a.num_wgs = (int)std::min<int64_t>(attention_slots(), a.work);
-  a.num_ranges = a.num_wgs;
+  a.num_wgs = plan.num_ranges;
+  a.num_ranges = plan.num_ranges;
   a.scale_log2 = scale * 1.4426950408889634f;
+  std::copy(plan.start, plan.start + plan.num_ranges, a.start);
   attention_kernel<<<a.num_wgs, kThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

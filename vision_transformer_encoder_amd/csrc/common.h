@@ -139,6 +139,17 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 }
 
 // 8 bf16 (one 16-byte load) as fp32.
+// Image of packed position t: the last j in [0, n) with cu[j] <= t (cu[0..n]
+// non-decreasing token offsets; empty images are skipped).  Binary search.
+__device__ __forceinline__ int image_of(const int32_t* __restrict__ cu, int n, int t) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 __device__ __forceinline__ void unpack8_bf16(uint4 w, float v[8]) {
   v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
   v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);

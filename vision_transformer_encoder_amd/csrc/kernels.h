@@ -33,18 +33,35 @@ hipError_t launch_bf16_gemm(const void* a, bool a_f32, const uint16_t* w, int M,
 hipError_t launch_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* pos, int T,
                          int heads, int head_dim, float theta, hipStream_t stream);
 
+// Stream-K plan of one attention launch, from the host copy of cu_seqlens:
+// the work per head (sum over windows of 256-query tiles x 64-key tiles),
+// one range of the work order per workgroup, and where each range starts
+// (its window and the position inside that window's (q tile, key tile)
+// list), so that the kernels never search the windows.
+constexpr int kAttnMaxRanges = 256;
+struct AttnRangeStart {
+  int32_t win;
+  int32_t rem;
+};
+struct AttnPlan {
+  int64_t work_per_head;
+  int num_ranges;
+  AttnRangeStart start[kAttnMaxRanges];
+};
+void plan_attention(const int32_t* cu_host, int num_seqs, int heads, AttnPlan* plan);
+
 // Stream-K attention: `partial` is device memory of attention_partial_bytes()
 // for the partials of items that the per-workgroup ranges cut; the launch
 // enqueues the main kernel and the combine kernel.
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             int64_t ld_qkv, uint16_t* o, int64_t ld_o, const int32_t* cu,
-                            int num_seqs, int total_tokens, int64_t work_per_head, int heads,
+                            int num_seqs, int total_tokens, const AttnPlan& plan, int heads,
                             float scale, float* partial, hipStream_t stream);
-// Sum over windows of (256-query tiles x 64-key tiles).
-int64_t attention_work_per_head(const int32_t* cu_host, int num_seqs);
 size_t attention_partial_bytes();
 
-hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_hw,
+// grid_hw [n][2] and cu [n + 1] (the token offsets of the images) describe
+// the same packing.
+hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_hw, const int32_t* cu,
                                   int num_images, int T, const uint16_t* gamma,
                                   const uint16_t* beta, float eps, uint16_t* out,
                                   hipStream_t stream);
@@ -56,7 +73,7 @@ hipError_t launch_geometry(const int32_t* grid_hw, int num_images, int T, int32_
 hipError_t launch_preprocess(const uint8_t* frames, int F, int H, int W, int Ho, int Wo, const float a[3],
                              const float b[3], float* out, hipStream_t stream);
 
-hipError_t launch_pos_interp(const uint16_t* table, int G, int D, const int32_t* grid_hw, int num_images, int T,
-                             uint16_t* out, int64_t ldo, hipStream_t stream);
+hipError_t launch_pos_interp(const uint16_t* table, int G, int D, const int32_t* grid_hw, const int32_t* cu,
+                             int num_images, int T, uint16_t* out, int64_t ldo, hipStream_t stream);
 
 }  // namespace vit

@@ -14,6 +14,7 @@ namespace vit {
 template <int NC>
 __global__ __launch_bounds__(256) void merge_layernorm_kernel(const uint16_t* __restrict__ x, int D,
                                                               const int32_t* __restrict__ grid_hw,
+                                                              const int32_t* __restrict__ cu,
                                                               int num_images, int TM,
                                                               const uint16_t* __restrict__ gamma,
                                                               const uint16_t* __restrict__ beta,
@@ -21,22 +22,16 @@ __global__ __launch_bounds__(256) void merge_layernorm_kernel(const uint16_t* __
   const int lane = threadIdx.x & 63;
   const int mrow = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (mrow >= TM) return;
-  // locate the image of this merged row
-  int tok0 = 0, mbase = 0, w = 2, local = mrow;
-  for (int j = 0; j < num_images; ++j) {
-    const int h = grid_hw[2 * j], ww = grid_hw[2 * j + 1];
-    const int nm = (h / 2) * (ww / 2);
-    if (mrow < mbase + nm) {
-      w = ww;
-      local = mrow - mbase;
-      break;
-    }
-    mbase += nm;
-    tok0 += h * ww;
-  }
+  // the image of this merged row: image j's merged rows start at cu[j] / 4
+  const int j = image_of(cu, num_images, 4 * mrow);
+  const int tok0 = cu[j], w = max(grid_hw[2 * j + 1], 2);
+  const int local = mrow - tok0 / 4;
   const int R = local / (w / 2), C = local % (w / 2);
-  const int src[4] = {tok0 + 2 * R * w + 2 * C, tok0 + 2 * R * w + 2 * C + 1, tok0 + (2 * R + 1) * w + 2 * C,
-                      tok0 + (2 * R + 1) * w + 2 * C + 1};
+  // clamped into the batch (only matters if the device grids disagreed with
+  // the validated host copy)
+  const int last = 4 * TM - 1;
+  const int src[4] = {min(tok0 + 2 * R * w + 2 * C, last), min(tok0 + 2 * R * w + 2 * C + 1, last),
+                      min(tok0 + (2 * R + 1) * w + 2 * C, last), min(tok0 + (2 * R + 1) * w + 2 * C + 1, last)};
   const int D4 = 4 * D;
   const int nchunk = D4 >> 3, cpd = D >> 3;
   // gamma and beta travel with the row (one memory round trip, not two)
@@ -101,7 +96,7 @@ __global__ __launch_bounds__(256) void merge_layernorm_kernel(const uint16_t* __
   }
 }
 
-hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_hw,
+hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_hw, const int32_t* cu,
                                   int num_images, int T, const uint16_t* gamma,
                                   const uint16_t* beta, float eps, uint16_t* out,
                                   hipStream_t stream) {
@@ -111,7 +106,7 @@ hipError_t launch_merge_layernorm(const uint16_t* x, int D, const int32_t* grid_
   const dim3 grid((TM + 3) / 4);
 #define VIT_ML(N)                                                                                      \
   case N:                                                                                             \
-    merge_layernorm_kernel<N><<<grid, 256, 0, stream>>>(x, D, grid_hw, num_images, TM, gamma, beta, \
+    merge_layernorm_kernel<N><<<grid, 256, 0, stream>>>(x, D, grid_hw, cu, num_images, TM, gamma, beta, \
                                                         eps, out);                                 \
     break;
   switch (nc) {
@@ -141,11 +136,7 @@ __global__ __launch_bounds__(256) void positions_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ pos) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
-  int lo = 0, hi = n - 1;  // last image j with cu[j] <= t
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
-  }
+  const int lo = image_of(cu, n, t);
   const int w = grid_hw[2 * lo + 1];
   const int local = t - cu[lo];
   pos[2 * t] = local / w;
@@ -176,23 +167,18 @@ hipError_t launch_geometry(const int32_t* grid_hw, int num_images, int T, int32_
 // one chunk per loop trip.
 template <int NC>
 __global__ __launch_bounds__(256) void pos_interp_kernel(const uint16_t* __restrict__ table, int G, int D,
-                                                         const int32_t* __restrict__ grid_hw, int num_images,
+                                                         const int32_t* __restrict__ grid_hw,
+                                                         const int32_t* __restrict__ cu, int num_images,
                                                          int T, uint16_t* __restrict__ out, int64_t ldo) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  int tok0 = 0, h = 1, w = 1;
-  for (int j = 0; j < num_images; ++j) {
-    const int hh = grid_hw[2 * j], ww = grid_hw[2 * j + 1];
-    if (t < tok0 + hh * ww) {
-      h = hh;
-      w = ww;
-      break;
-    }
-    tok0 += hh * ww;
-  }
-  const int local = t - tok0, r = local / w, c = local % w;
+  const int j = image_of(cu, num_images, t);
+  const int h = max(grid_hw[2 * j], 1), w = max(grid_hw[2 * j + 1], 1);
+  // (r, c) clamped into the table's sample range (only matters if the device
+  // grids disagreed with the validated host copy)
+  const int local = t - cu[j], r = min(local / w, h - 1), c = local % w;
   // (G-1) i is an exact f32 integer; the division is correctly rounded
   const float y = h > 1 ? ((float)(G - 1) * (float)r) / (float)(h - 1) : 0.0f;
   const float x = w > 1 ? ((float)(G - 1) * (float)c) / (float)(w - 1) : 0.0f;
@@ -267,19 +253,19 @@ __global__ __launch_bounds__(256) void pos_interp_kernel(const uint16_t* __restr
   }
 }
 
-hipError_t launch_pos_interp(const uint16_t* table, int G, int D, const int32_t* grid_hw, int num_images, int T,
-                             uint16_t* out, int64_t ldo, hipStream_t stream) {
+hipError_t launch_pos_interp(const uint16_t* table, int G, int D, const int32_t* grid_hw, const int32_t* cu,
+                             int num_images, int T, uint16_t* out, int64_t ldo, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const dim3 grid((T + 3) / 4);
 #define VIT_PI(N)                                                                                  \
   case N:                                                                                          \
-    pos_interp_kernel<N><<<grid, 256, 0, stream>>>(table, G, D, grid_hw, num_images, T, out, ldo); \
+    pos_interp_kernel<N><<<grid, 256, 0, stream>>>(table, G, D, grid_hw, cu, num_images, T, out, ldo); \
     break;
   switch ((D / 8 + 63) / 64) {
     VIT_PI(1) VIT_PI(2) VIT_PI(3) VIT_PI(4) VIT_PI(5) VIT_PI(6) VIT_PI(7) VIT_PI(8)
     VIT_PI(9) VIT_PI(10) VIT_PI(11) VIT_PI(12) VIT_PI(13) VIT_PI(14) VIT_PI(15) VIT_PI(16)
     default:
-      pos_interp_kernel<0><<<grid, 256, 0, stream>>>(table, G, D, grid_hw, num_images, T, out, ldo);
+      pos_interp_kernel<0><<<grid, 256, 0, stream>>>(table, G, D, grid_hw, cu, num_images, T, out, ldo);
   }
 #undef VIT_PI
   return hipGetLastError();
