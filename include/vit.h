@@ -224,6 +224,28 @@ int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64
                   vit_stream_t stream);
 
 /* ---------------------------------------------------------------------
+ * vit_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and errors as vit_attention,
+ * without the workspace.  The partial results live in the library's own
+ * array of vit_attention_noalloc_scratch_size() bytes (38.8 MB), one copy
+ * per device, taken from the code object when the library is first used
+ * on that device and held until the process ends; the need does not grow
+ * with the input (it holds the partials of at most 256 ranges), so no
+ * input is too large for it.  No call allocates (no hipMalloc / hipFree).
+ * Calls that overlap in time on one device share that array and race:
+ * serialise them (one stream, or events).  Nothing in the array needs to
+ * be zero on entry.  The first call on a device may return VIT_ERR_HIP if
+ * the array's address cannot be obtained there.
+ * ------------------------------------------------------------------- */
+size_t vit_attention_noalloc_scratch_size(void);
+int vit_attention_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          int64_t ld_qkv, uint16_t* o, int64_t ld_o,
+                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                          int num_seqs, int total_tokens, int num_heads, int head_dim,
+                          float softmax_scale, vit_stream_t stream);
+
+/* ---------------------------------------------------------------------
  * 2x2 spatial merge fused with the merger LayerNorm (FlashRT section 3
  * "2x2 patch merger"; spark_model page: spatial_merge_size 2).  For image j
  * with grid (h, w) = grid_hw[j] starting at token cu[j], merged row

@@ -138,6 +138,30 @@ def test_attention_validation(lib):
     assert call(cuh=empty, ns=0, T=0, ws=None) == OK
 
 
+def test_attention_noalloc_validation(lib):
+    """The workspace-free entry point validates like vit_attention (every
+    case here fails before the library looks at a device)."""
+    f = lib.vit_attention_noalloc
+    lib.vit_attention_noalloc_scratch_size.restype = ctypes.c_size_t
+    assert lib.vit_attention_noalloc_scratch_size() >= lib.vit_attention_workspace_size()
+    cu = _cu([0, 5, 9])
+
+    def call(q=A, ld=3456, o=D, cuh=cu, ns=2, T=9, hd=72, scale=0.1, cud=E):
+        return f(q, q + 2304, q + 4608, ld, o, 1152, cud, cuh, ns, T, 16, hd, ctypes.c_float(scale), None)
+
+    assert call(hd=64) == UNSUP
+    assert call(cuh=_cu([1, 5, 9])) == SEQ
+    assert call(T=10) == SEQ
+    assert call(o=A + 64) == ALIAS
+    assert call(cuh=None) == NULL
+    assert call(cud=None) == NULL
+    assert call(q=A + 8) == ALIGN
+    assert call(ld=3452) == ALIGN
+    assert call(ld=(1 << 24) + 8) == SHAPE
+    assert call(scale=float("inf")) == SHAPE
+    assert call(cuh=_cu([0]), ns=0, T=0) == OK
+
+
 def test_merge_validation_statuses(lib):
     f = lib.vit_merge2x2_layernorm
     grids = _cu([4, 6, 2, 2])

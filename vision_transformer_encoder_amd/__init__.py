@@ -24,7 +24,8 @@ __all__ = [
     "VitError", "require_library", "library_path", "declared_functions",
     "vit_abi_version", "vit_status_string", "vit_quant_fp8_block128", "vit_e4m3_encode",
     "vit_layernorm_quant_fp8", "vit_fp8_block128_gemm", "vit_bf16_gemm", "vit_rope2d",
-    "vit_attention", "vit_attention_workspace_size", "vit_merge2x2_layernorm", "vit_block_workspace_size", "vit_block_forward",
+    "vit_attention", "vit_attention_workspace_size", "vit_attention_noalloc",
+    "vit_attention_noalloc_scratch_size", "vit_merge2x2_layernorm", "vit_block_workspace_size", "vit_block_forward",
     "vit_encoder_workspace_size", "vit_encoder_forward", "BlockWeights", "MergerWeights",
     "EncoderWeights", "EPI_BIAS", "EPI_BIAS_RESIDUAL", "EPI_BIAS_GELU_FP8", "BEPI_BIAS",
     "BEPI_BIAS_GELU", "BEPI_BIAS_ADD",
@@ -88,6 +89,8 @@ _SIGS = {
     "vit_rope2d": (_I, [_P, _P, _I64, _P, _I, _I, _I, _F, _P]),
     "vit_attention_workspace_size": (_SZ, []),
     "vit_attention": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _P, _SZ, _P]),
+    "vit_attention_noalloc_scratch_size": (_SZ, []),
+    "vit_attention_noalloc": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _P]),
     "vit_merge2x2_layernorm": (_I, [_P, _I, _P, _P, _P, _I, _I, _P, _P, _F, _P, _P]),
     "vit_pos_embed_interp": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _I64, _P]),
     "vit_smart_resize": (_I, [_I, _I, _I, _I64, _I64, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
@@ -298,6 +301,26 @@ def vit_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens:
           len(cu_h) - 1, T, num_heads, head_dim, scale, _p(workspace), workspace.numel() * workspace.element_size(),
           _stream(q.device))
     return out
+
+
+def vit_attention_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Sequence[int],
+                          cu_seqlens_dev: torch.Tensor, out: torch.Tensor, num_heads: int = HEADS,
+                          head_dim: int = HEAD_DIM, softmax_scale: Optional[float] = None) -> torch.Tensor:
+    """vit_attention without a workspace: the library's own per-device
+    scratch holds the partials.  The caller passes the device cu_seqlens
+    and the output buffer; the call itself allocates nothing."""
+    ld = _row_ld(q)
+    if _row_ld(k) != ld or _row_ld(v) != ld:
+        raise ValueError("q, k, v must share a row stride")
+    cu_h, cu_ptr = _host_i32(cu_seqlens)
+    scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
+    _call("vit_attention_noalloc", _p(q), _p(k), _p(v), ld, _p(out), _row_ld(out), _p(cu_seqlens_dev), cu_ptr,
+          len(cu_h) - 1, q.shape[0], num_heads, head_dim, scale, _stream(q.device))
+    return out
+
+
+def vit_attention_noalloc_scratch_size() -> int:
+    return int(require_library().vit_attention_noalloc_scratch_size())
 
 
 def vit_attention_workspace_size() -> int:

@@ -437,8 +437,8 @@ size_t vit_attention_workspace_size(void) { return vit::attention_partial_bytes(
 }  // extern "C"
 
 namespace {
-// Validation of an attention call, everything but the workspace.  VIT_OK
-// with *nothing = true: nothing to enqueue.
+// Validation shared by vit_attention and vit_attention_noalloc (everything
+// but the workspace).  VIT_OK with *nothing = true: nothing to enqueue.
 int check_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv, const uint16_t* o,
                     int64_t ld_o, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
                     int total_tokens, int num_heads, int head_dim, float softmax_scale, bool* nothing) {
@@ -489,6 +489,27 @@ int vit_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64
   return hip_status(launch_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, num_seqs, total_tokens, plan,
                                      num_heads, softmax_scale, static_cast<float*>(workspace),
                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t vit_attention_noalloc_scratch_size(void) { return vit::attention_scratch_bytes(); }
+
+int vit_attention_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv, uint16_t* o,
+                          int64_t ld_o, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                          int num_seqs, int total_tokens, int num_heads, int head_dim, float softmax_scale,
+                          vit_stream_t stream) {
+  bool nothing = true;
+  const int st = check_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                 total_tokens, num_heads, head_dim, softmax_scale, &nothing);
+  if (st != VIT_OK || nothing) return st;
+  // the partials need at most attention_partial_bytes(), whatever the input
+  if (vit::attention_partial_bytes() > vit::attention_scratch_bytes()) return VIT_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* scratch = nullptr;
+  if (vit::attention_scratch(s, &scratch) != hipSuccess || !scratch) return VIT_ERR_HIP;
+  vit::AttnPlan plan;
+  vit::plan_attention(cu_seqlens_host, num_seqs, num_heads, &plan);
+  return hip_status(launch_attention(q, k, v, ld_qkv, o, ld_o, cu_seqlens_dev, num_seqs, total_tokens, plan,
+                                     num_heads, softmax_scale, scratch, s));
 }
 
 int vit_merge2x2_layernorm(const uint16_t* x, int D, const int32_t* grid_hw_dev, const int32_t* cu_seqlens_dev,

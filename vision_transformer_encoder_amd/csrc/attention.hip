@@ -58,6 +58,7 @@
 //    time is the same and the combine takes half again as long.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -700,6 +701,48 @@ __global__ __launch_bounds__(2 * kBQ) void attention_combine_kernel(AttnParams a
 }
 
 size_t attention_partial_bytes() { return (size_t)2 * kMaxRanges * kSlotFloats * sizeof(float); }
+
+// ---------------------------------------------------------------- no-allocation variant
+// The partials of vit_attention_noalloc live in this file-scope array, one
+// copy per device (38.8 MB: two slots of [74][256] fp32 for each of the at
+// most 256 stream-K ranges; the need does not grow with the input).  Host
+// code never uses its name as an address: the device address of each copy
+// is taken once per device with hipGetSymbolAddress and kept below.
+static __device__ __align__(256) float scratch[2 * kMaxRanges * kSlotFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+float* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+size_t attention_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t attention_scratch(hipStream_t stream, float** ptr) {
+  static_assert(sizeof(scratch) >= (size_t)2 * kMaxRanges * kSlotFloats * sizeof(float), "scratch too small");
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    // with that device current; the caller's current device is restored
+    int cur = -1;
+    hipError_t r = hipGetDevice(&cur);
+    if (r == hipSuccess && cur != dev) r = hipSetDevice(dev);
+    void* p = nullptr;
+    if (r == hipSuccess) r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r2 = hipSetDevice(cur);
+      if (r == hipSuccess) r = r2;
+    }
+    g_scratch_err[dev] = r;
+    g_scratch_ptr[dev] = r == hipSuccess ? static_cast<float*>(p) : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // Resident slots of the current device: one 512-thread workgroup per CU,
 // at most kMaxWorkgroups.

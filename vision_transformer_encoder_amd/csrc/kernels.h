@@ -58,6 +58,11 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
                             int num_seqs, int total_tokens, const AttnPlan& plan, int heads,
                             float scale, float* partial, hipStream_t stream);
 size_t attention_partial_bytes();
+// Device address (for the device `stream` runs on) of the library's own
+// copy of the attention partials, used by vit_attention_noalloc; set up on
+// the first call per device.
+hipError_t attention_scratch(hipStream_t stream, float** ptr);
+size_t attention_scratch_bytes();
 
 // grid_hw [n][2] and cu [n + 1] (the token offsets of the images) describe
 // the same packing.
