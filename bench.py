@@ -9,13 +9,17 @@ Prints ONE JSON line.  `value` is milliseconds per image (lower is better).
 The `roofline` object is the attention kernel (the tower's largest cost):
 algorithmic FLOPs per launch (4 * P^2 * 1152) over its average launch
 duration, measured here with HIP events on the stream it runs on, at the
-launch configuration the tower uses.  `kernels` gives the same for every
-kernel of the step.  `cpu_baseline` times the fp64 CPU oracle on a bounded
-sample of the same workload (one block, the patch embed and one merger at
-6256 patches) and scales it to the whole forward.
+launch configuration the tower uses; its fraction is given against the
+published bf16 peak and against the peak a dense-MFMA loop reaches on this
+chip in the same run (`measured_peaks`).  `kernels` gives the same for
+every kernel of the step.  `sizes` repeats the forward at 972, 1824, 3888
+and 6256 patches and on the packed 972 + 3888 + 1824 batch (eager and as
+one HIP graph), with the attention alone at each size.  `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of each workload (the
+per-config figures state what was timed and what was scaled).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload encoder_p6256]
-                       [--no-cpu-baseline] [--kernels/--no-kernels]
+                       [--no-cpu-baseline] [--no-kernels] [--no-sizes]
 """
 
 from __future__ import annotations
@@ -80,46 +84,120 @@ def encoder_flops(seq_lens, depth=27, n_mergers=4):
     return d
 
 
+def _host_info():
+    """Cores this process may run on, the BLAS numpy calls (vendor, version,
+    threads) and the CPU model."""
+    info = {"affinity_cores": len(os.sched_getaffinity(0))}
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(blas[0].get("num_threads", 1))
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    return info
+
+
 def cpu_baseline(grids, cfg):
-    """Time the fp64 oracle on two blocks, the patch embed and one merger of
-    the workload (about 14 s of CPU work at 6256 patches) and scale to the
-    whole forward (27 blocks, 4 mergers)."""
+    """The fp64 oracle (storage-emulating and pure modes) timed on the host
+    on a bounded sample of each workload, about 20-30 s of CPU work:
+    the single block (256 patches) and the attention-only case (1824
+    patches) whole; the FP8 GEMM sweep at M = 6256 whole (storage mode);
+    for the two full towers the patch embed, one block and one merger,
+    scaled to 27 blocks and 4 mergers (pure mode of the packed batch scaled
+    from its storage time by the single image's pure / storage ratio)."""
     import numpy as np
     import oracle as O
     import synth
     from oracle import inputs as OI
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    T = sum(h * w for h, w in grids)
-    pos, cu = O.positions_from_grids(grids), O.cu_seqlens_from_grids(grids)
-    bw = OI.block_weights(synth.block_params(cfg, 0))
-    for n in ("qkv", "proj", "fc1", "fc2"):
-        bw.fp8(n)  # weight preparation is not part of a forward
-    mw = OI.merger_weights(synth.merger_params(cfg, 0))
-    pp = synth.patch_params(cfg)
-    ew = O.EncoderWeights(patch_w=OI.dec(pp["patch_w"]), patch_b=OI.dec(pp["patch_b"]), blocks=[], mergers=[])
-    px = synth.pixels(cfg, T).astype(np.float64)
-    bw2 = OI.block_weights(synth.block_params(cfg, 1))
-    for n in ("qkv", "proj", "fc1", "fc2"):
-        bw2.fp8(n)
-    t0 = time.perf_counter()
-    x = O.patch_embed(px, ew)
-    t1 = time.perf_counter()
-    x = O.block_forward(x, bw, pos, cu)
-    x = O.block_forward(x, bw2, pos, cu)
-    t2 = time.perf_counter()
-    O.merger_forward(x, mw, grids)
-    t3 = time.perf_counter()
-    per_block = (t2 - t1) / 2
-    est_s = (t1 - t0) + 27 * per_block + 4 * (t3 - t2)
-    return {"value": est_s * 1e3 / len(grids), "unit": "ms/image", "cores": int(threads), "kind": "oracle",
-            "sample": f"patch embed + 2 of 27 blocks + 1 of 4 mergers at {T} patches "
-                      f"({t3 - t0:.1f} s measured: patch {t1 - t0:.2f} s, blocks {t2 - t1:.2f} s, "
-                      f"merger {t3 - t2:.2f} s), scaled to 27 blocks + 4 mergers",
-            "measured_s": round(t3 - t0, 2)}
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    def block_w(c, i):
+        w = OI.block_weights(synth.block_params(c, i))
+        for n in ("qkv", "proj", "fc1", "fc2"):
+            w.fp8(n)  # weight preparation is not part of a forward
+        return w
+
+    per = {}
+    t_all = time.perf_counter()
+    # configs[0]: one block, 16 x 16
+    g0 = [(16, 16)]
+    x0 = synth.bf16_bits_to_f64(synth.normal_bf16(0, "x", 0, (256, 1152)))
+    w0 = block_w(0, 0)
+    p0, c0 = O.positions_from_grids(g0), O.cu_seqlens_from_grids(g0)
+    per["block_p256"] = {m: round(1e3 * timed(lambda: O.block_forward(x0, w0, p0, c0, mode=m)), 1)
+                         for m in ("storage", "pure")}
+    per["block_p256"].update(unit="ms per block", timed="whole")
+    # configs[1]: attention only, 48 x 38 (the same in both modes)
+    g1 = [(48, 38)]
+    q1, k1, v1 = (synth.bf16_bits_to_f64(synth.normal_bf16(1, t, 0, (1824, 1152))) for t in ("q", "k", "v"))
+    ta = timed(lambda: O.attention(q1, k1, v1, O.cu_seqlens_from_grids(g1)))
+    per["attention_p1824"] = {"storage": round(1e3 * ta, 1), "pure": round(1e3 * ta, 1),
+                              "unit": "ms per call", "timed": "whole (attention has no storage points)"}
+    # configs[2]: the four FP8 GEMMs at M = 6256 with their epilogues
+    a_c, a_s = O.quantize_block128(synth.bf16_bits_to_f64(synth.normal_bf16(2, "a", 0, (6256, 1152))), 1)
+    h_c, h_s = O.quantize_block128(synth.bf16_bits_to_f64(synth.normal_bf16(2, "a", 1, (6256, 4352))), 1)
+    wb = block_w(2, 0)
+    res = synth.bf16_bits_to_f64(synth.normal_bf16(2, "residual", 0, (6256, 1152)))
+
+    def sweep():
+        for n, (ac, as_), N, epi in (("qkv", (a_c, a_s), 3456, O.EPI_BIAS), ("proj", (a_c, a_s), 1152,
+                                                                              O.EPI_BIAS_RESIDUAL),
+                                     ("fc1", (a_c, a_s), 4304, O.EPI_BIAS_GELU_FP8),
+                                     ("fc2", (h_c, h_s), 1152, O.EPI_BIAS_RESIDUAL)):
+            f = wb.fp8(n)
+            O.fp8_gemm_epilogue(O.fp8_block128_gemm(ac, as_, f.codes, f.scales), N, epi,
+                                bias=getattr(wb, n + "_b"), residual=res)
+    per["gemm_sweep_m6256"] = {"storage": round(1e3 * timed(sweep), 1), "unit": "ms per sweep (4 GEMMs)",
+                               "timed": "whole, storage mode (pure differs only in the bf16 rounding of "
+                                        "the outputs; not timed separately)"}
+    # configs[3] / [4]: the towers, sampled
+    for name, c, gr in (("encoder_p6256", 3, [(46, 136)]), ("encoder_varlen_6684", 4, [(18, 54), (36, 108),
+                                                                                      (24, 76)])):
+        T = sum(h * w for h, w in gr)
+        pos, cu = O.positions_from_grids(gr), O.cu_seqlens_from_grids(gr)
+        pp = synth.patch_params(c)
+        ew = O.EncoderWeights(patch_w=OI.dec(pp["patch_w"]), patch_b=OI.dec(pp["patch_b"]), blocks=[], mergers=[])
+        px = synth.pixels(c, T).astype(np.float64)
+        bw = block_w(c, 0)
+        mw = OI.merger_weights(synth.merger_params(c, 0))
+        rec = {"unit": "ms per image", "images": len(gr)}
+        for m in (("storage", "pure") if c == 3 else ("storage",)):
+            box = {}
+            tp = timed(lambda: box.update(x=O.patch_embed(px, ew, mode=m)))
+            tb = timed(lambda: box.update(x=O.block_forward(box["x"], bw, pos, cu, mode=m)))
+            tm = timed(lambda: O.merger_forward(box["x"], mw, gr, mode=m))
+            total = tp + 27 * tb + 4 * tm
+            rec[m] = round(1e3 * total / len(gr), 1)
+            rec[m + "_measured_s"] = {"patch_embed": round(tp, 2), "block": round(tb, 2), "merger": round(tm, 2)}
+        rec["timed"] = "patch embed + 1 of 27 blocks + 1 of 4 mergers, scaled to 27 blocks + 4 mergers"
+        per[name] = rec
+    v = per["encoder_varlen_6684"]
+    s3 = per["encoder_p6256"]
+    v["pure"] = round(v["storage"] * s3["pure"] / s3["storage"], 1)
+    v["timed"] += "; pure mode scaled by the 6256-patch pure / storage ratio"
+    measured = time.perf_counter() - t_all
+    info = _host_info()
+    used = min(info["affinity_cores"], info.get("blas_threads", info["affinity_cores"]))
+    head = per["encoder_p6256"]
+    return {"value": head["storage"], "unit": "ms/image", "cores": used, "kind": "oracle",
+            "sample": ("27-block tower at 6256 patches, storage-emulating fp64 oracle: patch embed + 1 of 27 "
+                       "blocks + 1 of 4 mergers timed, scaled to 27 blocks + 4 mergers; every workload in "
+                       "per_config"),
+            "measured_s": round(measured, 1), "per_config": per, **info,
+            "threads_note": "BLAS calls use blas_threads threads; numpy's elementwise work runs on one"}
 
 
 def main() -> int:
@@ -130,6 +208,8 @@ def main() -> int:
     ap.add_argument("--workload", default="encoder_p6256", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel event timings")
+    ap.add_argument("--no-sizes", action="store_true",
+                    help="skip the forward at the other image sizes (972 / 1824 / 3888 patches, varlen batch)")
     ap.add_argument("--bf16-blocks", type=int, default=0,
                     help="precision variant: the first N blocks run LayerNorm and GEMMs in bf16 (the pages keep 3)")
     ap.add_argument("--fp8-mergers", action="store_true", help="precision variant: FP8 merger linears")
@@ -222,16 +302,22 @@ def main() -> int:
 
     flops = encoder_flops([h * w for h, w in grids])
     seq = [h * w for h, w in grids]
+    peaks = measured_peaks(dev)
     kernels = {}
     roofline = None
     if not args.no_kernels:
-        kernels = time_in_context(vit, W, px, grids, g_dev, dev, max(1, min(args.steps, 5)))
+        kernels = time_in_context(vit, W, px, grids, g_dev, dev, max(1, min(args.steps, 5)), peaks)
         a = kernels["attention"]
         roofline = {"bound": "mfma", "achieved": a["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(a["tflops"] / PEAK_BF16_TFLOPS, 4),
                     "traffic": traffic_from_profiles("attention"),
                     "kernel": "attention_kernel", "avg_launch_us": a["us"],
-                    "algorithmic_flop_per_launch": a["flop"]}
+                    "algorithmic_flop_per_launch": a["flop"],
+                    "peak_measured": peaks["bf16_tflops"],
+                    "frac_measured": round(a["tflops"] / peaks["bf16_tflops"], 4)}
+    sizes = None
+    if not args.no_sizes and not variant:
+        sizes = time_sizes(vit, W, dev, peaks, main=(args.workload, ms_per_step))
 
     line = {
         "metric": METRIC,
@@ -258,6 +344,9 @@ def main() -> int:
         "precision": {"bf16_blocks": args.bf16_blocks, "fp8_mergers": bool(args.fp8_mergers)},
         "position_table": "learned 48x48, resampled per image" if args.pos_table else None,
     }
+    line["measured_peaks"] = peaks
+    if sizes is not None:
+        line["sizes"] = sizes
     if roofline is not None:
         line["roofline"] = roofline
         line["kernels"] = kernels
@@ -272,16 +361,161 @@ def main() -> int:
     return 0 if ok else 1
 
 
-def _kernel_record(us, per_step, work, unit):
+def _kernel_record(us, per_step, work, unit, peaks=None):
     r = {"us": round(us, 2), "per_step": per_step}
     if unit == "B":
         gbs = work / (us * 1e-6) / 1e9
         r.update(bytes=int(work), gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 3))
+        if peaks:
+            r["frac_hbm_measured"] = round(gbs / peaks["copy_gbs"], 3)
     else:
         tf = work / (us * 1e-6) / 1e12
         peak = PEAK_FP8_TFLOPS if unit == "F8" else PEAK_BF16_TFLOPS
         r.update(flop=int(work), tflops=round(tf, 1), frac_mfma=round(tf / peak, 4))
+        if peaks:
+            r["frac_mfma_measured"] = round(tf / peaks["fp8_tflops" if unit == "F8" else "bf16_tflops"], 4)
     return r
+
+
+def measured_peaks(dev):
+    """What this chip reaches in this run: dense MFMA loops of the two
+    matrix instructions the kernels use (libvit_peak.so, two waves per SIMD
+    on every CU) and a 2 x 512 MB device copy (read + write bytes)."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "vision_transformer_encoder_amd", "libvit_peak.so"))
+    lib.vit_peak_mfma.restype = ctypes.c_int
+    lib.vit_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.vit_peak_mfma_flops.restype = ctypes.c_double
+    lib.vit_peak_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wgs = 2 * cus
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {"compute_units": cus}
+    for kind, name, iters in ((0, "bf16_tflops", 20000), (1, "fp8_tflops", 10000)):
+        best = 0.0
+        for rep in range(4):  # the first launch warms the clocks up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if lib.vit_peak_mfma(kind, iters, wgs, out.data_ptr(), ctypes.c_void_p(stream.cuda_stream)) != 0:
+                raise RuntimeError("MFMA peak probe failed to launch")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep > 0:
+                best = max(best, lib.vit_peak_mfma_flops(kind, iters, wgs) / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        res[name] = round(best, 1)
+    src = torch.empty(256 * 1024 * 1024, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    best = 0.0
+    for rep in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rep > 0:
+            best = max(best, 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    res["copy_gbs"] = round(best, 1)
+    res["frac_of_published"] = {"bf16": round(res["bf16_tflops"] / PEAK_BF16_TFLOPS, 3),
+                                "fp8": round(res["fp8_tflops"] / PEAK_FP8_TFLOPS, 3),
+                                "hbm": round(res["copy_gbs"] / PEAK_HBM_GBS, 3)}
+    print(f"[bench] measured peaks: {res}", file=sys.stderr, flush=True)
+    del src, dst
+    return res
+
+
+SIZES = ("encoder_p972", "encoder_p1824", "encoder_p3888", "encoder_p6256", "encoder_varlen_6684")
+
+
+def time_sizes(vit, W, dev, peaks, main=None, steps=10, warmup=3):
+    """The whole forward at each image size of the pages' resolution table
+    and on the packed batch: ms per step eager and replayed as one HIP
+    graph, whole-forward TFLOP/s, and the attention alone (main + combine
+    kernels, `steps` back-to-back launches in a graph) with its fraction of
+    the published and the measured bf16 peak.  Weights are those of the
+    headline workload (timing does not depend on their values)."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in SIZES:
+        grids = WORKLOADS[name]["grids"]
+        seq = [h * w for h, w in grids]
+        T = sum(seq)
+        px = torch.from_numpy(synth.pixels(WORKLOADS[name]["cfg"], T)).to(dev)
+        g_dev = torch.from_numpy(np.asarray(grids, np.int32).reshape(-1, 2)).to(dev)
+        ws = torch.empty(vit.vit_encoder_workspace_size(T, len(grids)), dtype=torch.uint8, device=dev)
+        o = torch.empty((4, T // 4, 4096), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            vit.vit_encoder_forward(W, px, grids, workspace=ws, out=o, grid_dev=g_dev)
+
+        def timed(run):
+            for _ in range(warmup):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+
+        eager = timed(step)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        replay = timed(graph.replay)
+        del graph
+        # attention alone at this size
+        H = 1152
+        qkv = torch.randn((T, 3 * H), device=dev).to(torch.bfloat16)
+        cu = np.concatenate([[0], np.cumsum(seq)]).astype(np.int32)
+        cu_dev = torch.from_numpy(cu).to(dev)
+        ao = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        aws = torch.empty(vit.vit_attention_workspace_size(), dtype=torch.uint8, device=dev)
+
+        def attn():
+            vit.vit_attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], cu, cu_seqlens_dev=cu_dev, out=ao,
+                              workspace=aws)
+
+        attn()
+        torch.cuda.synchronize()
+        ag = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ag):
+            for _ in range(steps):
+                attn()
+        ag.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ag.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        a_us = e0.elapsed_time(e1) * 1e3 / steps
+        del ag
+        fl = encoder_flops(seq)
+        a_tf = sum(4 * p * p * H for p in seq) / (a_us * 1e-6) / 1e12
+        ms = eager
+        if main is not None and main[0] == name:
+            ms = main[1]  # the headline measurement of this run
+        out[name] = {"patches": T, "images": len(grids), "ms_per_step_eager": round(eager, 3),
+                     "ms_per_step_graph": round(replay, 3), "ms_per_image": round(ms / len(grids), 3),
+                     "tflops": round(fl["total"] / (ms * 1e-3) / 1e12, 1),
+                     "attention_us": round(a_us, 1), "attention_tflops": round(a_tf, 1),
+                     "attention_frac": round(a_tf / PEAK_BF16_TFLOPS, 4),
+                     "attention_frac_measured": round(a_tf / peaks["bf16_tflops"], 4)}
+        print(f"[bench] size {name}: {out[name]}", file=sys.stderr, flush=True)
+        del px, ws, o, qkv, ao, aws
+    return out
 
 
 def kernel_work(T, seq):
@@ -306,7 +540,7 @@ def kernel_work(T, seq):
     }
 
 
-def time_in_context(vit, W, px, grids, g_dev, dev, steps):
+def time_in_context(vit, W, px, grids, g_dev, dev, steps, peaks=None):
     """Average duration of every kernel inside the running forward: the
     tower is run as the sequence of per-op C-ABI calls vit_encoder_forward
     makes (same kernels, shapes and order, on the same stream), with HIP
@@ -386,7 +620,7 @@ def time_in_context(vit, W, px, grids, g_dev, dev, steps):
                 m = W.mergers[taps[b + 1]].t
                 y = timed("merge_layernorm",
                           lambda: vit.vit_merge2x2_layernorm(x, grids, m["m_ln_g"], m["m_ln_b"], grid_dev=g_dev,
-                                                             out=y_m))
+                                                             out=y_m, cu_dev=cu_dev))
                 hh = timed("merger_fc1_bf16", lambda: vit.vit_bf16_gemm(y, m["m_fc1_w"], bias=m["m_fc1_b"],
                                                                         epilogue=vit.BEPI_BIAS_GELU, out=h_m))
                 timed("merger_fc2_bf16", lambda: vit.vit_bf16_gemm(hh, m["m_fc2_w"], bias=m["m_fc2_b"], out=z_m))
@@ -396,7 +630,7 @@ def time_in_context(vit, W, px, grids, g_dev, dev, steps):
     for name, sp in spans.items():
         us = sum(e0.elapsed_time(e1) for e0, e1 in sp) * 1e3 / len(sp)
         w, unit, per_step = work[name]
-        res[name] = _kernel_record(us, per_step, w, unit)
+        res[name] = _kernel_record(us, per_step, w, unit, peaks)
         print(f"[bench] in forward: {name}: {res[name]}", file=sys.stderr, flush=True)
     return res
 
@@ -462,8 +696,8 @@ def time_kernels(vit, W, T, grids, dev, reps, seq, only=None, eager=False):
                          gemm(H, 4304), "F8", B),
         "patch_embed_bf16": (lambda: vit.vit_bf16_gemm(px, W.patch["patch_w"], bias=W.patch["patch_b"], out=xp),
                              gemm(H, 1536), "F16", 1),
-        "merge_layernorm": (lambda: vit.vit_merge2x2_layernorm(x, grids, m["m_ln_g"], m["m_ln_b"], grid_dev=g_dev),
-                            2 * T * H * 2, "B", 4),
+        "merge_layernorm": (lambda: vit.vit_merge2x2_layernorm(x, grids, m["m_ln_g"], m["m_ln_b"], grid_dev=g_dev,
+                                                               cu_dev=cu_dev), 2 * T * H * 2, "B", 4),
         "merger_fc1_bf16": (lambda: vit.vit_bf16_gemm(mln, m["m_fc1_w"], bias=m["m_fc1_b"],
                                                       epilogue=vit.BEPI_BIAS_GELU, out=mh),
                             2 * TM * 4608 * 4608, "F16", 4),
@@ -479,7 +713,8 @@ def time_kernels(vit, W, T, grids, dev, reps, seq, only=None, eager=False):
                            724 * 2172 * 3 + 6256 * 1536 * 4, "B", 0)
     # the learned position table resampled to the grids (only with --pos-table
     # in the forward): the table read once, the [T, 1152] result written
-    cases["pos_embed_interp"] = (lambda: vit.vit_pos_embed_interp(ptab, grids, out=pe_out),
+    cases["pos_embed_interp"] = (lambda: vit.vit_pos_embed_interp(ptab, grids, out=pe_out, grid_dev=g_dev,
+                                                                  cu_dev=cu_dev),
                                  48 * 48 * H * 2 + T * H * 2, "B", 0)
     # a plain copy of known size: the reference for the HBM byte counters
     cases["copy_calibration"] = (lambda: cpy_dst.copy_(cpy_src), 2 * cpy_src.numel() * 2, "B", 0)

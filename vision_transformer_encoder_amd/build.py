@@ -3,7 +3,8 @@
 Usage: ``python -m vision_transformer_encoder_amd.build`` or ``build()``.
 Every call recompiles every source (no caching): objects go to
 ``vision_transformer_encoder_amd/_build/``, the library to
-``vision_transformer_encoder_amd/libvit.so``.
+``vision_transformer_encoder_amd/libvit.so``; the benchmark's MFMA peak probe
+(csrc/peak) to ``vision_transformer_encoder_amd/libvit_peak.so``.
 """
 
 from __future__ import annotations
@@ -22,6 +23,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvit.so")
+# measurement probe of the benchmark (dense MFMA issue rate), not the tower
+PEAK_SRC = os.path.join(CSRC, "peak", "mfma_peak.hip")
+PEAK_LIB = os.path.join(PKG, "libvit_peak.so")
 
 SOURCES = ["quant.hip", "rope.hip", "attention.hip", "gemm.hip", "merge.hip", "preprocess.hip", "abi.cpp"]
 
@@ -85,8 +89,13 @@ def build(verbose: bool = True) -> str:
     except OSError as e:
         raise RuntimeError(f"linked library does not load: {e}") from None
     shutil.move(tmp, LIB)
+    tmp = PEAK_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", "-x", "hip", PEAK_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PEAK_SRC}:\n{r.stdout}\n{r.stderr}")
+    shutil.move(tmp, PEAK_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAK_LIB}")
     return LIB
 
 

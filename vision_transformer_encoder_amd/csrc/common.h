@@ -18,7 +18,8 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kE4M3Max = 448.0f;
-// Block maxima below 2^-116 give a zero scale: 448 / amax would overflow fp32.
+// Block maxima below 2^-116 give a zero scale; from 2^-116 up, amax / 448
+// (>= 2^-124.8) and 448 / amax (<= 2^124.8) are normal, finite fp32 values.
 constexpr float kTinyAmax = 0x1p-116f;
 
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
