@@ -194,3 +194,30 @@ def test_attention_peaky_logits(gpu, grids, kind):
     torch.cuda.synchronize()
     ref = O.attention(q, k, v, cu)
     assert_close(host_f64(o), ref, MAX_REL, MIN_COS, f"attention peaky {kind} T={T}")
+
+
+@pytest.mark.parametrize("shards", [2, 8, 16], ids=["8_heads", "2_heads", "1_head"])
+def test_attention_head_shard(gpu, shards):
+    """Attention on a head shard: the share of one of `shards` GPUs in a head
+    split of the 16 heads (q, k, v and o as column slices of the full
+    [T, 3456] / [T, 1152] buffers, num_heads = 16 / shards).  Every shard is
+    compared with the oracle on its heads, and the shards put together with
+    the oracle on all 16."""
+    grids = [(46, 136)]
+    T, qkv, q, k, vf = _attention_case(gpu, grids)
+    cu = synth.cu_seqlens(grids)
+    H = 16 // shards
+    W = 72 * H
+    out = torch.empty((T, 1152), dtype=torch.bfloat16, device=gpu)
+    announce(f"vit_attention head shards: {shards} x {H} heads, T={T}")
+    for s in range(shards):
+        c = slice(s * W, (s + 1) * W)
+        vit.vit_attention(qkv[:, c], qkv[:, 1152 + s * W:1152 + (s + 1) * W], qkv[:, 2304 + s * W:2304 + (s + 1) * W],
+                          cu, num_heads=H, out=out[:, c])
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    for s in (0, shards - 1):
+        c = slice(s * W, (s + 1) * W)
+        ref = O.attention(q[:, c], k[:, c], vf[:, c], cu, num_heads=H)
+        assert_close(got[:, c], ref, MAX_REL, MIN_COS, f"attention shard {s} of {shards}")
+    assert_close(got, O.attention(q, k, vf, cu), MAX_REL, MIN_COS, f"attention, {shards} shards put together")
