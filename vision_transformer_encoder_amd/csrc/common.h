@@ -36,13 +36,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 __device__ __forceinline__ uint16_t f2bf(float a) { return (uint16_t)(pack_bf16x2(a, 0.0f) & 0xffffu); }
 
-// fp32 -> OCP E4M3FN, nearest-even, saturating at +-448 (v_cvt_pk_fp8_f32 on
-// gfx950 rounds to nearest-even; the clamp makes saturation explicit).
-__device__ __forceinline__ float e4m3_clamp(float x) { return fminf(fmaxf(x, -kE4M3Max), kE4M3Max); }
+// fp32 -> OCP E4M3FN, nearest-even (v_cvt_pk_fp8_f32 on gfx950).  The
+// conversion itself gives 448 up to 464 (where the next E4M3 step would lie)
+// and the NaN code above it, so e4m3x4 is exact saturation only for inputs of
+// magnitude at most 464.  The block quantisers feed it x * (448 / amax) with
+// |x| <= amax, at most 448 (1 + 2^-23) after the two roundings.  Arbitrary
+// values go through e4m3x4_sat, which clamps to +-448 first.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  int v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
-  v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), v, true);
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
   return (uint32_t)v;
+}
+__device__ __forceinline__ float e4m3_clamp(float x) { return fminf(fmaxf(x, -kE4M3Max), kE4M3Max); }
+__device__ __forceinline__ uint32_t e4m3x4_sat(float a, float b, float c, float d) {
+  return e4m3x4(e4m3_clamp(a), e4m3_clamp(b), e4m3_clamp(c), e4m3_clamp(d));
 }
 
 // Block-128 scale: s = amax / 448 and inv = 448 / amax, both correctly
@@ -139,7 +146,6 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// 8 bf16 (one 16-byte load) as fp32.
 // Image of packed position t: the last j in [0, n) with cu[j] <= t (cu[0..n]
 // non-decreasing token offsets; empty images are skipped).  Binary search.
 __device__ __forceinline__ int image_of(const int32_t* __restrict__ cu, int n, int t) {
@@ -151,6 +157,7 @@ __device__ __forceinline__ int image_of(const int32_t* __restrict__ cu, int n, i
   return lo;
 }
 
+// 8 bf16 (one 16-byte load) as fp32.
 __device__ __forceinline__ void unpack8_bf16(uint4 w, float v[8]) {
   v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
   v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);

@@ -163,9 +163,9 @@ __global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restric
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i + 4 <= n) {
     float4 v = *reinterpret_cast<const float4*>(x + i);
-    *reinterpret_cast<uint32_t*>(codes + i) = e4m3x4(v.x, v.y, v.z, v.w);
+    *reinterpret_cast<uint32_t*>(codes + i) = e4m3x4_sat(v.x, v.y, v.z, v.w);
   } else {
-    for (int64_t j = i; j < n; ++j) codes[j] = (uint8_t)(e4m3x4(x[j], 0.0f, 0.0f, 0.0f) & 0xff);
+    for (int64_t j = i; j < n; ++j) codes[j] = (uint8_t)(e4m3x4_sat(x[j], 0.0f, 0.0f, 0.0f) & 0xff);
   }
 }
 
