@@ -90,6 +90,10 @@ BF16_SHAPES = [  # (name, M, N, K, a_f32, epilogue)
     ("merger_fc1", 1564, 4608, 4608, False, 1),
     ("merger_fc2", 1564, 4096, 4608, False, 0),
     ("ragged", 77, 130, 72, False, 1),
+    # the 256-wide tile path (bf16 A, N % 256 == 0, K % 192 == 0): a ragged
+    # last row tile, one round of three K steps, and no bias
+    ("wide_ragged_m", 77, 512, 384, False, 1),
+    ("wide_three_k_steps", 300, 256, 192, False, 0),
 ]
 
 
@@ -108,7 +112,9 @@ def test_bf16_gemm(gpu, name, M, N, K, a_f32, epi):
     w_bits = synth.normal_bf16(3, "w", seed, (N, K), std=0.02)
     b_bits = synth.normal_bf16(3, "bias", seed, (N,), std=0.01)
     add_bits = synth.normal_bf16(3, "pos_embed", seed, (M, N)) if epi == 2 else None
-    out = vit.vit_bf16_gemm(a_dev, dev_bf16(w_bits, gpu), bias=dev_bf16(b_bits, gpu),
+    if name == "wide_three_k_steps":
+        b_bits = np.zeros_like(b_bits)
+    out = vit.vit_bf16_gemm(a_dev, dev_bf16(w_bits, gpu), bias=None if name == "wide_three_k_steps" else dev_bf16(b_bits, gpu),
                             add=dev_bf16(add_bits, gpu) if add_bits is not None else None, epilogue=epi)
     c = O.bf16_gemm(a_val, synth.bf16_bits_to_f64(w_bits), synth.bf16_bits_to_f64(b_bits))
     if epi == 1:

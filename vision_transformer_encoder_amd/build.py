@@ -27,7 +27,8 @@ LIB = os.path.join(PKG, "libvit.so")
 PEAK_SRC = os.path.join(CSRC, "peak", "mfma_peak.hip")
 PEAK_LIB = os.path.join(PKG, "libvit_peak.so")
 
-SOURCES = ["quant.hip", "rope.hip", "attention.hip", "gemm.hip", "merge.hip", "preprocess.hip", "abi.cpp"]
+SOURCES = ["quant.hip", "rope.hip", "attention.hip", "gemm.hip", "gemm_wide.hip", "merge.hip", "preprocess.hip",
+           "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -521,6 +521,8 @@ hipError_t launch_bf16_gemm(const void* a, bool a_f32, const uint16_t* w, int M,
                             const uint16_t* bias, const uint16_t* add, int epilogue,
                             uint16_t* out, int64_t ld_out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  if (!a_f32 && epilogue != 2 && bf16_gemm_wide_fits(N, K, ld_out, out, bias))
+    return launch_bf16_gemm_wide(static_cast<const uint16_t*>(a), w, M, N, K, bias, epilogue, out, ld_out, stream);
   const int n_tiles = (N + kBN - 1) / kBN, m_tiles = (M + kBM - 1) / kBM;
   const int nblocks = n_tiles * m_tiles;
   const dim3 grid(nblocks);

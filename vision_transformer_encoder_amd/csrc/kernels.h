@@ -30,6 +30,12 @@ hipError_t launch_bf16_gemm(const void* a, bool a_f32, const uint16_t* w, int M,
                             const uint16_t* bias, const uint16_t* add, int epilogue,
                             uint16_t* out, int64_t ld_out, hipStream_t stream);
 
+// The 256-wide tile bf16 GEMM (gemm_wide.hip) for bf16 A: usable when
+// bf16_gemm_wide_fits(); epilogue 0 (bias) or 1 (bias + GELU).
+bool bf16_gemm_wide_fits(int N, int K, int64_t ld_out, const void* out, const void* bias);
+hipError_t launch_bf16_gemm_wide(const uint16_t* a, const uint16_t* w, int M, int N, int K, const uint16_t* bias,
+                                 int epilogue, uint16_t* out, int64_t ld_out, hipStream_t stream);
+
 hipError_t launch_rope2d(uint16_t* q, uint16_t* k, int64_t ld, const int32_t* pos, int T,
                          int heads, int head_dim, float theta, hipStream_t stream);
 
