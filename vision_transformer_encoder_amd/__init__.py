@@ -33,7 +33,9 @@ __all__ = [
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_PKG)
-library_path = os.path.join(_PKG, "libvit.so")
+# VIT_LIBRARY names another build of the same library (a host-sanitizer
+# build, for instance); by default the in-tree libvit.so
+library_path = os.environ.get("VIT_LIBRARY") or os.path.join(_PKG, "libvit.so")
 header_path = os.path.join(_ROOT, "include", "vit.h")
 
 ABI_VERSION = 5  # VIT_ABI_VERSION of the include/vit.h these signatures follow
