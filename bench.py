@@ -52,11 +52,17 @@ WORKLOADS = {
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and layout are left out,
+    so that a comment edit does not orphan counters taken on the same code."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "vision_transformer_encoder_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            text = open(os.path.join(csrc, f), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(f.encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -3,7 +3,9 @@
 //    fused into the GEMM; section 3: GELU fused with the FP8 quant of the fc2
 //    input) for qkv / proj / fc1 / fc2;
 //  * bf16 (section 4: patch embed and mergers stay bf16) for the patch
-//    embedding (fp32 pixels rounded on load) and the merger MLPs.
+//    embedding (fp32 pixels rounded on load) and the merger MLPs; shapes
+//    with bf16 activations, N % 256 == 0 and K % 192 == 0 (the mergers) go
+//    to the 256-wide tile kernel of gemm_wide.hip.
 // Weights are [N, K] row-major (spark_model "layers/vision_encoder.rs":
 // C[M,N] = A[M,K] @ B[N,K]^T + bias), activations [M, K]; both K-contiguous.
 //
@@ -25,9 +27,11 @@
 //    all happen there, and every global store is a full 16-byte run, so
 //    rows are written with whole cache lines.
 //  * Tile order is XCD-aware: workgroups are dealt round-robin to the 8
-//    XCDs, so block id b is remapped to a logical tile such that each XCD
-//    owns a contiguous range of M tiles (with all N tiles): each activation
-//    tile is fetched by one XCD's L2 only.
+//    XCDs, so block id b is remapped to a logical tile index such that each
+//    XCD owns a contiguous range of the tile order, and that order walks the
+//    N tiles in groups of at most 12 (every M tile of one group, then the
+//    next group): the workgroups resident on one XCD share a few activation
+//    tiles and one group's weight slice in its L2.
 #include "common.h"
 #include "kernels.h"
 
