@@ -122,3 +122,22 @@ def test_bf16_gemm(gpu, name, M, N, K, a_f32, epi):
     if epi == 2:
         c = c + synth.bf16_bits_to_f64(add_bits)
     assert_close(host_f64(out), O.bf16(c), TOL_GEMM, 0.9999, name)
+
+
+@pytest.mark.parametrize("pad", [24, 2], ids=["wide_path", "fallback_path"])
+def test_bf16_gemm_into_row_strided_output(gpu, pad):
+    """bf16 GEMM into the first N columns of a wider buffer: a row stride the
+    256-wide tile path takes (a multiple of 4) and one it leaves to the
+    128 x 128 kernel; the columns past N keep their contents."""
+    M, N, K = 200, 512, 192
+    a_bits = synth.normal_bf16(3, "a", 11, (M, K))
+    w_bits = synth.normal_bf16(3, "w", 11, (N, K), std=0.02)
+    b_bits = synth.normal_bf16(3, "bias", 11, (N,), std=0.01)
+    buf = torch.full((M, N + pad), 7.0, dtype=torch.bfloat16, device=gpu)
+    announce(f"vit_bf16_gemm into a row stride of {N + pad}")
+    vit.vit_bf16_gemm(dev_bf16(a_bits, gpu), dev_bf16(w_bits, gpu), bias=dev_bf16(b_bits, gpu),
+                      epilogue=vit.BEPI_BIAS_GELU, out=buf[:, :N])
+    c = O.gelu_tanh(O.bf16_gemm(synth.bf16_bits_to_f64(a_bits), synth.bf16_bits_to_f64(w_bits),
+                                synth.bf16_bits_to_f64(b_bits)))
+    assert_close(host_f64(buf[:, :N]), O.bf16(c), TOL_GEMM, 0.9999, f"row stride {N + pad}")
+    assert torch.all(buf[:, N:] == 7.0)
