@@ -105,6 +105,46 @@ def test_block_zero_weights_identity(gpu):
     assert torch.equal(x.view(torch.int16), dev_bf16(x_bits, gpu).view(torch.int16))
 
 
+@pytest.mark.parametrize("grids", [[(6, 8), (12, 21)], [(18, 54), (36, 108), (24, 76)]], ids=["two_images_300",
+                                                                                              "varlen_6684"])
+def test_block_forward_bit_exact_with_its_entry_points(gpu, grids):
+    """The FP8 block forward is the chain of its C-ABI steps, byte for byte:
+    LayerNorm-quant, QKV GEMM, RoPE, attention, row quantisation, projection
+    + residual, LayerNorm-quant, FC1 + GELU-quant, FC2 + residual."""
+    T = sum(h * w for h, w in grids)
+    params = synth.block_params(4, 1)
+    w = vit.BlockWeights(params, gpu)
+    t = w.t
+    x_bits = synth.normal_bf16(4, "x", 1, (T, 1152))
+    pos = torch.from_numpy(synth.positions(grids)).to(gpu)
+    cu = synth.cu_seqlens(grids)
+    cu_dev = torch.from_numpy(cu).to(gpu)
+    announce(f"vit_block_forward vs its entry points T={T}")
+    x_blk = dev_bf16(x_bits, gpu).clone()
+    vit.vit_block_forward(w, x_blk, pos, cu, cu_seqlens_dev=cu_dev)
+
+    x = dev_bf16(x_bits, gpu).clone()
+    c1, s1 = vit.vit_layernorm_quant_fp8(x, t["ln1_g"], t["ln1_b"])
+    qkv = vit.vit_fp8_block128_gemm(c1, s1, w.q["qkv"][0], w.q["qkv"][1], 3456, 1152, bias=t["qkv_b"])
+    vit.vit_rope2d(qkv[:, :1152], qkv[:, 1152:2304], pos)
+    # the block's softmax scale is the fp32 1 / sqrtf(72), one ulp above the
+    # binding's default (1 / sqrt(72) rounded from double)
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(72.0)))
+    o = vit.vit_attention(qkv[:, :1152], qkv[:, 1152:2304], qkv[:, 2304:], cu, cu_seqlens_dev=cu_dev,
+                          softmax_scale=scale)
+    oc, os_ = vit.vit_quant_fp8_block128(o, block_rows=1)
+    vit.vit_fp8_block128_gemm(oc, os_, w.q["proj"][0], w.q["proj"][1], 1152, 1152, bias=t["proj_b"], residual=x,
+                              epilogue=vit.EPI_BIAS_RESIDUAL, out=x)
+    c2, s2 = vit.vit_layernorm_quant_fp8(x, t["ln2_g"], t["ln2_b"])
+    hc, hs = vit.vit_fp8_block128_gemm(c2, s2, w.q["fc1"][0], w.q["fc1"][1], 4304, 1152, bias=t["fc1_b"],
+                                       epilogue=vit.EPI_BIAS_GELU_FP8)
+    vit.vit_fp8_block128_gemm(hc, hs, w.q["fc2"][0], w.q["fc2"][1], 1152, 4304, bias=t["fc2_b"], residual=x,
+                              epilogue=vit.EPI_BIAS_RESIDUAL, out=x)
+    torch.cuda.synchronize()
+    n = int((x_blk.view(torch.int16) != x.view(torch.int16)).sum())
+    assert n == 0, f"block forward and its entry points differ in {n} of {x.numel()} elements"
+
+
 @pytest.fixture(scope="module")
 def small_tower(gpu):
     ep = synth.encoder_params(0)
