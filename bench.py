@@ -138,7 +138,7 @@ def cpu_baseline(grids, cfg):
 
     per = {}
     t_all = time.perf_counter()
-    # configs[0]: one block, 16 x 16
+    # one block on a 16 x 16 grid (256 patches)
     g0 = [(16, 16)]
     x0 = synth.bf16_bits_to_f64(synth.normal_bf16(0, "x", 0, (256, 1152)))
     w0 = block_w(0, 0)
@@ -146,13 +146,13 @@ def cpu_baseline(grids, cfg):
     per["block_p256"] = {m: round(1e3 * timed(lambda: O.block_forward(x0, w0, p0, c0, mode=m)), 1)
                          for m in ("storage", "pure")}
     per["block_p256"].update(unit="ms per block", timed="whole")
-    # configs[1]: attention only, 48 x 38 (the same in both modes)
+    # attention alone on a 48 x 38 grid (1824 patches; the same in both modes)
     g1 = [(48, 38)]
     q1, k1, v1 = (synth.bf16_bits_to_f64(synth.normal_bf16(1, t, 0, (1824, 1152))) for t in ("q", "k", "v"))
     ta = timed(lambda: O.attention(q1, k1, v1, O.cu_seqlens_from_grids(g1)))
     per["attention_p1824"] = {"storage": round(1e3 * ta, 1), "pure": round(1e3 * ta, 1),
                               "unit": "ms per call", "timed": "whole (attention has no storage points)"}
-    # configs[2]: the four FP8 GEMMs at M = 6256 with their epilogues
+    # the four FP8 GEMMs of a block at M = 6256 with their epilogues
     a_c, a_s = O.quantize_block128(synth.bf16_bits_to_f64(synth.normal_bf16(2, "a", 0, (6256, 1152))), 1)
     h_c, h_s = O.quantize_block128(synth.bf16_bits_to_f64(synth.normal_bf16(2, "a", 1, (6256, 4352))), 1)
     wb = block_w(2, 0)
@@ -169,7 +169,7 @@ def cpu_baseline(grids, cfg):
     per["gemm_sweep_m6256"] = {"storage": round(1e3 * timed(sweep), 1), "unit": "ms per sweep (4 GEMMs)",
                                "timed": "whole, storage mode (pure differs only in the bf16 rounding of "
                                         "the outputs; not timed separately)"}
-    # configs[3] / [4]: the towers, sampled
+    # the towers (one 46 x 136 image; the 972 + 3888 + 1824 batch), sampled
     for name, c, gr in (("encoder_p6256", 3, [(46, 136)]), ("encoder_varlen_6684", 4, [(18, 54), (36, 108),
                                                                                       (24, 76)])):
         T = sum(h * w for h, w in gr)
@@ -226,7 +226,7 @@ def main() -> int:
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--kernel", default=None,
                     help="only launch this kernel of the step (eagerly, --kernel-reps times) and report its "
-                         "timing: the driver of the per-kernel counter profiles")
+                         "timing: the program the per-kernel counter profiles run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs the tower on one GPU; --gpus {args.gpus} is not supported "
