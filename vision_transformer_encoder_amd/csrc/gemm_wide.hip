@@ -4,19 +4,19 @@
 // activations with N % 256 == 0 and K % 192 == 0, the other cases go to
 // bf16_gemm_kernel (gemm.hip).
 //
-// gfx950 design: 256 (n) x 128 (m) tiles, 4 waves of 128 (n) x 64 (m) on
-// v_mfma_f32_16x16x32_bf16 (operand lane l: row l % 16, k 8 (l / 16) .. +8;
-// result lane l: rows n 4 (l / 16) + 0..3 of column m l % 16).  Per 32 k a
-// wave reads 8 W and 4 A fragments for 32 MFMAs, a quarter fewer LDS bytes
-// per multiply-add than 64 x 64 waves, and a tile takes a quarter fewer
-// global bytes per multiply-add than a 128 x 128 one.  The 1564 x 4608
-// merger fc1 is 234 tiles, one 4-wave workgroup per CU, so the latency of
-// the global loads is hidden by depth, not by other waves: each 64-deep K
-// step is copied global -> LDS directly (buffer loads with the LDS as
-// destination, no registers) two steps before it is used, into a ring of
-// three stages; an XOR swizzle chosen on the global side keeps the 16-byte
-// operand reads conflict-free in 128-byte rows.  The epilogue writes from
-// the accumulators (four features of a token per 8-byte store).
+// gfx950 design: 256 (n) x 128 (m) tiles, 8 waves of 64 (n) x 64 (m) (two
+// per SIMD, 4 x 2 over the tile) on v_mfma_f32_16x16x32_bf16 (operand lane
+// l: row l % 16, k 8 (l / 16) .. +8; result lane l: rows n 4 (l / 16) +
+// 0..3 of column m l % 16).  A tile takes a quarter fewer global bytes per
+// multiply-add than a 128 x 128 one.  The 1564 x 4608 merger fc1 is 234
+// tiles, one workgroup per CU: the latency of the global loads is hidden by
+// depth, each 64-deep K step being copied global -> LDS directly (buffer
+// loads with the LDS as destination, no registers) two steps before it is
+// used, into a ring of three stages, and the LDS reads of one wave hide
+// behind the MFMAs of the other wave on its SIMD.  An XOR swizzle chosen on
+// the global side keeps the 16-byte operand reads conflict-free in 128-byte
+// rows.  The epilogue writes from the accumulators (four features of a
+// token per 8-byte store).
 #include "common.h"
 #include "kernels.h"
 
@@ -30,8 +30,11 @@ constexpr int kStageW = kBN * kRowB;
 constexpr int kStageA = kBM * kRowB;
 }  // namespace
 
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+
 // Global -> LDS copy of one K step of a tile: wave instruction j of wave w
-// fills LDS bytes [1024 (w + 4 j), +1024), i.e. rows 8 (w + 4 j) .. +8.
+// fills LDS bytes [1024 (w + 8 j), +1024), i.e. rows 8 (w + 8 j) .. +8.
 // Lane l lands at row 8 (w + 4 j) + l / 8, 16-byte slot p = l % 8, and
 // loads the row's chunk p ^ ((row / 2) % 8) (the same 128-byte line): slot
 // p of row r holds chunk p ^ ((r / 2) % 8).
@@ -47,7 +50,7 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* stage, int r, int c)
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256) void bf16_gemm_wide_kernel(const uint16_t* __restrict__ a,
+__global__ __launch_bounds__(kThreads) void bf16_gemm_wide_kernel(const uint16_t* __restrict__ a,
                                                              const uint16_t* __restrict__ w, int M, int N, int K,
                                                              int n_tiles, int nblocks, int group_n,
                                                              const uint16_t* __restrict__ bias, uint16_t* out,
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(256) void bf16_gemm_wide_kernel(const uint16_t* __r
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave & 3, wm = wave >> 2;
   const int l16 = lane & 15, lg = lane >> 4;
   const int lb = xcd_logical_block(blockIdx.x, nblocks);
   int m_tile, n_tile;
@@ -72,36 +75,35 @@ __global__ __launch_bounds__(256) void bf16_gemm_wide_kernel(const uint16_t* __r
       const_cast<uint16_t*>(w + (size_t)n0 * K), (short)0, kBN * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a + (size_t)m0 * K), (short)0, min(M - m0, kBM) * K * 2, 0x00020000);
-  uint32_t w_off[8], a_off[4];
+  uint32_t w_off[4], a_off[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w_off[j] = swz_off(8 * (wave + 4 * j) + (lane >> 3), lane, K);
+  for (int j = 0; j < 4; ++j) w_off[j] = swz_off(8 * (wave + 8 * j) + (lane >> 3), lane, K);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 8 * (wave + 4 * j) + (lane >> 3);
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * (wave + 8 * j) + (lane >> 3);
     const int rc = min(m0 + r, M - 1) - m0;
     a_off[j] = ((uint32_t)rc * (uint32_t)K + 8 * ((lane & 7) ^ ((r >> 1) & 7))) * 2;
   }
   auto copy_step = [&](uint8_t* ws, uint8_t* as, int ks) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, ws + 1024 * (wave + 4 * j), 16, (int)w_off[j], ks * 128, 0, 0);
-#pragma unroll
     for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, as + 1024 * (wave + 4 * j), 16, (int)a_off[j], ks * 128, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, ws + 1024 * (wave + 8 * j), 16, (int)w_off[j], ks * 128, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, as + 1024 * (wave + 8 * j), 16, (int)a_off[j], ks * 128, 0, 0);
   };
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{};
-  // one K step from a stage: per 32 k, the 4 A fragments, then the 8 W
-  // fragments, each read kFA - 1 = 2 ahead of its 4 MFMAs (deeper read-ahead
-  // measured the same)
+  // one K step from a stage: per 32 k, the 4 A fragments, then the 4 W
+  // fragments, each read kFA - 1 = 2 ahead of its 4 MFMAs
   constexpr int kFA = 3;
   auto compute = [&](const uint8_t* ws, const uint8_t* as) {
-    const int wr = 128 * wn + l16, ar = 64 * wm + l16;
-    auto w_frag = [&](int i) { return lds_frag(ws, wr + 16 * (i & 7), 4 * (i >> 3) + lg); };  // i = 8 kk + ns
+    const int wr = 64 * wn + l16, ar = 64 * wm + l16;
+    auto w_frag = [&](int i) { return lds_frag(ws, wr + 16 * (i & 3), 4 * (i >> 2) + lg); };  // i = 4 kk + ns
     bf16x8_t wf[kFA];
 #pragma unroll
     for (int i = 0; i < kFA - 1; ++i) wf[i] = w_frag(i);
@@ -109,10 +111,10 @@ __global__ __launch_bounds__(256) void bf16_gemm_wide_kernel(const uint16_t* __r
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) aop[0][ms] = lds_frag(as, ar + 16 * ms, lg);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = i >> 3, ns = i & 7;
-      if (i + kFA - 1 < 16) wf[(i + kFA - 1) % kFA] = w_frag(i + kFA - 1);
-      if (i == 2) {
+    for (int i = 0; i < 8; ++i) {
+      const int kk = i >> 2, ns = i & 3;
+      if (i + kFA - 1 < 8) wf[(i + kFA - 1) % kFA] = w_frag(i + kFA - 1);
+      if (i == 1) {
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) aop[1][ms] = lds_frag(as, ar + 16 * ms, 4 + lg);
       }
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(256) void bf16_gemm_wide_kernel(const uint16_t* __r
   };
 
   // Step s reads stage s % 3.  Its copy was issued two steps earlier; each
-  // wave waits for its own copy (all but the 12 copies of step s + 1) and
+  // wave waits for its own copy (all but the 6 copies of step s + 1) and
   // for its LDS reads of step s - 1, then the barrier: the stage is whole,
   // and stage (s + 2) % 3, read at step s - 1, is free for the next copy.
   // K steps come in threes (K % 192 == 0), so every step has the same shape:
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(256) void bf16_gemm_wide_kernel(const uint16_t* __r
   copy_step(w_s0, a_s0, 0);
   copy_step(w_s1, a_s1, 1);
   auto step = [&](int ks, const uint8_t* ws, const uint8_t* as, uint8_t* wn2, uint8_t* an2) {
-    asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     copy_step(wn2, an2, min(ks + 2, last));
     compute(ws, as);
   };
@@ -146,13 +148,13 @@ __global__ __launch_bounds__(256) void bf16_gemm_wide_kernel(const uint16_t* __r
   // the surplus copies land before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // epilogue from the accumulators: lane holds features n0 + 128 wn + 16 ns
+  // epilogue from the accumulators: lane holds features n0 + 64 wn + 16 ns
   // + 4 (lane / 16) + 0..3 of token m0 + 64 wm + 16 ms + lane % 16; four
   // consecutive features are one 8-byte store (the 16 lanes of a token
   // row group write 32 contiguous bytes per instruction)
 #pragma unroll
-  for (int ns = 0; ns < 8; ++ns) {
-    const int n = n0 + 128 * wn + 16 * ns + 4 * lg;
+  for (int ns = 0; ns < 4; ++ns) {
+    const int n = n0 + 64 * wn + 16 * ns + 4 * lg;
     float b4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (bias) {
       const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
@@ -190,9 +192,9 @@ hipError_t launch_bf16_gemm_wide(const uint16_t* a, const uint16_t* w, int M, in
   // many W bytes (4 x 256 rows) as A bytes (7-8 x 128 rows)
   const int group_n = min(4, n_tiles);
   if (epilogue == 0)
-    bf16_gemm_wide_kernel<0><<<nblocks, 256, 0, stream>>>(a, w, M, N, K, n_tiles, nblocks, group_n, bias, out, ld_out);
+    bf16_gemm_wide_kernel<0><<<nblocks, kThreads, 0, stream>>>(a, w, M, N, K, n_tiles, nblocks, group_n, bias, out, ld_out);
   else if (epilogue == 1)
-    bf16_gemm_wide_kernel<1><<<nblocks, 256, 0, stream>>>(a, w, M, N, K, n_tiles, nblocks, group_n, bias, out, ld_out);
+    bf16_gemm_wide_kernel<1><<<nblocks, kThreads, 0, stream>>>(a, w, M, N, K, n_tiles, nblocks, group_n, bias, out, ld_out);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
