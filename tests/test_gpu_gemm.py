@@ -141,3 +141,54 @@ def test_bf16_gemm_into_row_strided_output(gpu, pad):
                                 synth.bf16_bits_to_f64(b_bits)))
     assert_close(host_f64(buf[:, :N]), O.bf16(c), TOL_GEMM, 0.9999, f"row stride {N + pad}")
     assert torch.all(buf[:, N:] == 7.0)
+
+
+# Small M takes other tilings (64-token FP8 tiles when 128-token ones would
+# give at most one workgroup per CU; 64 x 64 bf16 tiles when the 256 x 128
+# ones would fill at most half the CUs).  Every output is the same chain of
+# MFMAs and FMAs in either tiling, so the rows of a small-M call equal, byte
+# for byte, the same rows of a large-M call on the same operands.
+FP8_TILE_SHAPES = [  # (name, N, K, epilogue)
+    ("qkv", 3456, 1152, O.EPI_BIAS),
+    ("proj", 1152, 1152, O.EPI_BIAS_RESIDUAL),
+    ("fc1", 4304, 1152, O.EPI_BIAS_GELU_FP8),
+    ("fc2", 1152, 4304, O.EPI_BIAS_RESIDUAL),
+]
+
+
+@pytest.mark.parametrize("name,N,K,epi", FP8_TILE_SHAPES, ids=[s[0] for s in FP8_TILE_SHAPES])
+def test_fp8_gemm_tilings_agree(gpu, name, N, K, epi):
+    M = 6256
+    d = _operands(gpu, M, N, K, 4000 + N + K)
+    res = d["r"] if epi == O.EPI_BIAS_RESIDUAL else None
+
+    def run(m):
+        if epi == O.EPI_BIAS_GELU_FP8:
+            c, s, p = vit.vit_fp8_block128_gemm(d["a_c"][:m], d["a_s"][:m], d["w_c"], d["w_s"], N, K, bias=d["b"],
+                                                epilogue=epi, prequant=True)
+            return [host_u8(c), host_f64(s), host_f64(p)]
+        o = vit.vit_fp8_block128_gemm(d["a_c"][:m], d["a_s"][:m], d["w_c"], d["w_s"], N, K, bias=d["b"],
+                                      residual=None if res is None else res[:m], epilogue=epi)
+        return [o.view(torch.int16).cpu().numpy()]
+
+    announce(f"vit_fp8_block128_gemm {name} tilings: M={M} against M=601, 64, 1")
+    full = run(M)
+    for m in (601, 64, 1):
+        for got, ref in zip(run(m), full):
+            assert np.array_equal(got, ref[:m]), f"{name}: rows of M={m} differ from the same rows at M={M}"
+
+
+BF16_TILE_SHAPES = [("merger_fc1", 4608, 4608, 1), ("merger_fc2", 4096, 4608, 0)]
+
+
+@pytest.mark.parametrize("name,N,K,epi", BF16_TILE_SHAPES, ids=[s[0] for s in BF16_TILE_SHAPES])
+def test_bf16_gemm_tilings_agree(gpu, name, N, K, epi):
+    M = 1564
+    a = dev_bf16(synth.normal_bf16(3, "a", 5000 + N, (M, K)), gpu)
+    w = dev_bf16(synth.normal_bf16(3, "w", 5000 + N, (N, K), std=0.02), gpu)
+    b = dev_bf16(synth.normal_bf16(3, "bias", 5000 + N, (N,), std=0.01), gpu)
+    announce(f"vit_bf16_gemm {name} tilings: M={M} against M=451, 243, 1")
+    full = vit.vit_bf16_gemm(a, w, bias=b, epilogue=epi).view(torch.int16).cpu().numpy()
+    for m in (451, 243, 1):
+        got = vit.vit_bf16_gemm(a[:m], w, bias=b, epilogue=epi).view(torch.int16).cpu().numpy()
+        assert np.array_equal(got, full[:m]), f"{name}: rows of M={m} differ from the same rows at M={M}"

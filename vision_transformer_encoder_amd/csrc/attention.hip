@@ -744,22 +744,25 @@ hipError_t attention_scratch(hipStream_t stream, float** ptr) {
   return hipSuccess;
 }
 
-// Resident slots of the current device: one 512-thread workgroup per CU,
-// at most kMaxWorkgroups.
-static int attention_slots() {
+// Compute units of the current device (256 if the query fails), cached per
+// device.
+int device_cu_count() {
   static std::atomic<int> cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxWorkgroups;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
   if (dev < 64) {
     const int c = cache[dev].load(std::memory_order_relaxed);
     if (c > 0) return c;
   }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  const int slots = std::min(cus, kMaxWorkgroups);
-  if (dev < 64) cache[dev].store(slots, std::memory_order_relaxed);
-  return slots;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
+
+// Resident slots of the current device: one 512-thread workgroup per CU,
+// at most kMaxWorkgroups.
+static int attention_slots() { return std::min(device_cu_count(), kMaxWorkgroups); }
 
 // Host plan of the stream-K split.  The work order of one head lists, per
 // window, its q tiles x key tiles; the whole order is heads x that list,

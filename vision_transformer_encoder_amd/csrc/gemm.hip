@@ -12,7 +12,9 @@
 // gfx950 design: 256 threads = 4 waves on a 128 (n) x 128 (m) output tile,
 // 2 x 2 waves of 64 x 64, v_mfma_f32_32x32x64_f8f6f4 (FP8) or
 // v_mfma_f32_32x32x16_bf16, the weight as MFMA A operand and the activation
-// as B operand.
+// as B operand.  When M is small enough that 128-token tiles would give at
+// most one workgroup per CU, the FP8 GEMM takes 128 x 64 tiles (waves of
+// 64 x 32) instead: each output is the same chain of MFMAs and FMAs.
 //  * FP8 block scaling: each 128-deep K block is one MFMA chain started from
 //    zero (the MFMA's internal sum is not fp32-exact, so partial sums are
 //    promoted every 128 K), then acc += partial * sA[m, kb] * sW[n/128, kb]
@@ -55,12 +57,13 @@ __device__ __forceinline__ i32x8_t lds_read32(const uint8_t* p) {
   return r;
 }
 
-// Park the 64x64 fp32 accumulators of this wave in the LDS C tile (row = m
-// local, column = n local).
-__device__ __forceinline__ void park_acc(float* c_lds, const f32x16_t acc[2][2], int wn, int wm, int l32, int g) {
+// Park the 64 x 32 MT fp32 accumulators of this wave in the LDS C tile
+// (row = m local, column = n local).
+template <int MT>
+__device__ __forceinline__ void park_acc(float* c_lds, const f32x16_t acc[2][MT], int wn, int wm, int l32, int g) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int ml = 64 * wm + 32 * mt + l32;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int ml = 32 * MT * wm + 32 * mt + l32;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
@@ -80,16 +83,24 @@ __device__ __forceinline__ void park_acc(float* c_lds, const f32x16_t acc[2][2],
 __device__ __forceinline__ void tile_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ============================================================ FP8 block-128
-template <int EPI>
+// BM = 128 or 64 tokens per tile: 2 x 2 waves of 64 (n) x BM / 2 (m).  The
+// 64-token tiles are for small M, where 128-token tiles would leave CUs
+// idle; every output sees the same MFMAs, promotions and epilogue either way.
+template <int EPI, int BM>
 __global__ __launch_bounds__(256) void fp8_gemm_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ a_scales, const uint8_t* __restrict__ w,
     const float* __restrict__ w_scales, int M, int N, int Np, int Kp, int n_tiles, int nblocks, int group_n,
     const uint16_t* __restrict__ bias, const uint16_t* residual, uint16_t* out,
     uint8_t* __restrict__ out_codes, float* __restrict__ out_scales, float* __restrict__ prequant) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileB];  // A x2, W x2; C tile after the loop
-  __shared__ float sa_lds[2][kBM];
+  constexpr int MT = BM / 64;             // 32-row m sub-tiles per wave
+  constexpr int NA = BM / 32;             // A rows loaded per thread and step
+  constexpr int kTileA = BM * kLS;
+  constexpr int kPasses = BM / 16;        // epilogue rows per thread
+  // A x2, W x2; the C tile after the loop
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kTileA + 2 * kTileB];
+  __shared__ float sa_lds[2][BM];
   uint8_t* a_lds = smem;
-  uint8_t* w_lds = smem + 2 * kTileB;
+  uint8_t* w_lds = smem + 2 * kTileA;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
@@ -97,7 +108,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
   const int lb = xcd_logical_block(blockIdx.x, nblocks);
   int m_tile, n_tile;
   grouped_tile(lb, nblocks / n_tiles, n_tiles, group_n, m_tile, n_tile);
-  const int n0 = n_tile * kBN, m0 = m_tile * kBM;
+  const int n0 = n_tile * kBN, m0 = m_tile * BM;
   const int Kb = Kp >> 7;
 
   // per-thread load slots: rows lrow + 32i, 16 bytes at lcol, as 32-bit
@@ -105,23 +116,23 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
   const int lrow = tid >> 3, lcol = (tid & 7) * 16;
   const uint8_t* a_tile = a + (size_t)m0 * Kp;
   const uint8_t* w_tile = w + (size_t)n0 * Kp;
-  uint32_t a_off[4], w_off[4];
+  uint32_t a_off[NA], w_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a_off[i] = (uint32_t)(min(m0 + lrow + 32 * i, M - 1) - m0) * (uint32_t)Kp + lcol;
+    if (i < NA) a_off[i] = (uint32_t)(min(m0 + lrow + 32 * i, M - 1) - m0) * (uint32_t)Kp + lcol;
     w_off[i] = (uint32_t)(lrow + 32 * i) * (uint32_t)Kp + lcol;
   }
-  const float* sa_ptr = a_scales + (size_t)min(m0 + (tid & 127), M - 1) * Kb;
+  const float* sa_ptr = a_scales + (size_t)min(m0 + (tid & (BM - 1)), M - 1) * Kb;
   const float* sw_ptr = w_scales + (size_t)n_tile * Kb;
 
-  u32x4_t ra[4], rw[4];
+  u32x4_t ra[NA], rw[4];
   float rs = 0.0f;
   auto gload = [&](int kb) {
     const uint8_t* ak = a_tile + kb * kRowB;
     const uint8_t* wk = w_tile + kb * kRowB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4_t*>(ak + a_off[i]);
+      if (i < NA) ra[i] = *reinterpret_cast<const u32x4_t*>(ak + a_off[i]);
       rw[i] = *reinterpret_cast<const u32x4_t*>(wk + w_off[i]);
     }
     rs = sa_ptr[kb];
@@ -130,17 +141,17 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = lrow + 32 * i;
-      *reinterpret_cast<u32x4_t*>(a_lds + buf * kTileB + row * kLS + lcol) = ra[i];
+      if (i < NA) *reinterpret_cast<u32x4_t*>(a_lds + buf * kTileA + row * kLS + lcol) = ra[i];
       *reinterpret_cast<u32x4_t*>(w_lds + buf * kTileB + row * kLS + lcol) = rw[i];
     }
-    if (tid < kBM) sa_lds[buf][tid] = rs;
+    if (tid < BM) sa_lds[buf][tid] = rs;
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][MT];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < MT; ++j) acc[i][j] = f32x16_t{};
 
   gload(0);
   lstore(0);
@@ -151,21 +162,21 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
     if (kb + 1 < Kb) gload(kb + 1);
     const float sw = sw_ptr[kb];
     const uint8_t* wl = w_lds + buf * kTileB + (64 * wn + l32) * kLS + 32 * g;
-    const uint8_t* al = a_lds + buf * kTileB + (64 * wm + l32) * kLS + 32 * g;
-    i32x8_t wop[2][2], aop[2][2];
+    const uint8_t* al = a_lds + buf * kTileA + (32 * MT * wm + l32) * kLS + 32 * g;
+    i32x8_t wop[2][2], aop[MT][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         wop[t][kh] = lds_read32(wl + 32 * t * kLS + 64 * kh);
-        aop[t][kh] = lds_read32(al + 32 * t * kLS + 64 * kh);
+        if (t < MT) aop[t][kh] = lds_read32(al + 32 * t * kLS + 64 * kh);
       }
     }
-    f32x16_t part[2][2];
+    f32x16_t part[2][MT];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         part[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[nt][0], aop[mt][0], f32x16_t{}, 0, 0,
                                                                        0, 0, 0, 0);
       }
@@ -173,18 +184,18 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         part[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[nt][1], aop[mt][1], part[nt][mt], 0,
                                                                        0, 0, 0, 0, 0);
       }
     }
-    float coef[2];
+    float coef[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) coef[mt] = sa_lds[buf][64 * wm + 32 * mt + l32] * sw;
+    for (int mt = 0; mt < MT; ++mt) coef[mt] = sa_lds[buf][32 * MT * wm + 32 * mt + l32] * sw;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nt][mt][r] = fmaf(part[nt][mt][r], coef[mt], acc[nt][mt][r]);
     if (kb + 1 < Kb) lstore(buf ^ 1);
@@ -210,28 +221,28 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
       for (int j = 0; j < 8; ++j) b8[j] = (n + j < N) ? bf2f(bias[n + j]) : 0.0f;
     }
   }
-  uint4 res8[8];
+  uint4 res8[kPasses];
   if constexpr (EPI == 1) {
     if (vec) {
 #pragma unroll
-      for (int pass = 0; pass < 8; ++pass) {
+      for (int pass = 0; pass < kPasses; ++pass) {
         const int m = min(m0 + (tid >> 4) + 16 * pass, M - 1);
         res8[pass] = *reinterpret_cast<const uint4*>(residual + (int64_t)m * N + n);
       }
     }
   }
   float* c_lds = reinterpret_cast<float*>(smem);
-  park_acc(c_lds, acc, wn, wm, l32, g);
+  park_acc<MT>(c_lds, acc, wn, wm, l32, g);
   tile_barrier();
-  float4 cv[8][2];
+  float4 cv[kPasses][2];
 #pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int ml = (tid >> 4) + 16 * pass;
     cv[pass][0] = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc);
     cv[pass][1] = *reinterpret_cast<const float4*>(c_lds + ml * kCS + cc + 4);
   }
 #pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int m = m0 + (tid >> 4) + 16 * pass;
     const float4 c0 = cv[pass][0], c1 = cv[pass][1];
     float y[8] = {c0.x + b8[0], c0.y + b8[1], c0.z + b8[2], c0.w + b8[3],
@@ -309,28 +320,28 @@ hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_scales, const uint8_
   if (M == 0) return hipSuccess;
   const int Kp = (K + 127) / 128 * 128;
   const int Np = (N + 127) / 128 * 128;
-  const int n_tiles = Np / kBN, m_tiles = (M + kBM - 1) / kBM;
+  const int n_tiles = Np / kBN;
+  // 64-token tiles when 128-token tiles would give at most one workgroup per
+  // CU: twice the workgroups, two per CU, for the same bytes
+  const bool small = n_tiles * ((M + 127) / 128) <= device_cu_count();
+  const int m_tiles = small ? (M + 63) / 64 : (M + 127) / 128;
   const int nblocks = n_tiles * m_tiles;
+  const int group_n = gemm_group_n(n_tiles);
   const dim3 grid(nblocks);
-  switch (epilogue) {
-    case 0:
-      fp8_gemm_kernel<0><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks,
-                                                   gemm_group_n(n_tiles), bias, residual, out, out_codes,
-                                                   out_scales, prequant);
-      break;
-    case 1:
-      fp8_gemm_kernel<1><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks,
-                                                   gemm_group_n(n_tiles), bias, residual, out, out_codes,
-                                                   out_scales, prequant);
-      break;
-    case 2:
-      fp8_gemm_kernel<2><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks,
-                                                   gemm_group_n(n_tiles), bias, residual, out, out_codes,
-                                                   out_scales, prequant);
-      break;
+#define VIT_FP8_GEMM_LAUNCH(E, B)                                                                              \
+  fp8_gemm_kernel<E, B><<<grid, 256, 0, stream>>>(a, a_scales, w, w_scales, M, N, Np, Kp, n_tiles, nblocks, \
+                                                  group_n, bias, residual, out, out_codes, out_scales, prequant)
+  switch (epilogue * 2 + (small ? 1 : 0)) {
+    case 0: VIT_FP8_GEMM_LAUNCH(0, 128); break;
+    case 1: VIT_FP8_GEMM_LAUNCH(0, 64); break;
+    case 2: VIT_FP8_GEMM_LAUNCH(1, 128); break;
+    case 3: VIT_FP8_GEMM_LAUNCH(1, 64); break;
+    case 4: VIT_FP8_GEMM_LAUNCH(2, 128); break;
+    case 5: VIT_FP8_GEMM_LAUNCH(2, 64); break;
     default:
       return hipErrorInvalidValue;
   }
+#undef VIT_FP8_GEMM_LAUNCH
   return hipGetLastError();
 }
 
@@ -473,7 +484,7 @@ __global__ __launch_bounds__(256) void bf16_gemm_kernel(const void* __restrict__
     }
   }
   float* c_lds = reinterpret_cast<float*>(smem);
-  park_acc(c_lds, acc, wn, wm, l32, g);
+  park_acc<2>(c_lds, acc, wn, wm, l32, g);
   tile_barrier();
   float4 cv[8][2];
 #pragma unroll

@@ -20,6 +20,9 @@ hipError_t launch_layernorm_quant(const uint16_t* x, int64_t ldx, const uint16_t
 hipError_t launch_layernorm_bf16(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* beta,
                                  float eps, int M, int D, uint16_t* out, int64_t ldo, hipStream_t stream);
 
+// Compute units of the current device, cached per device (attention.hip).
+int device_cu_count();
+
 hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
                            const float* w_scales, int M, int N, int K, const uint16_t* bias,
                            const uint16_t* residual, int epilogue, uint16_t* out,
