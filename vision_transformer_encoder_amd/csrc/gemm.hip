@@ -153,13 +153,8 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < MT; ++j) acc[i][j] = f32x16_t{};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < Kb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < Kb) gload(kb + 1);
+  // one 128-deep K block from LDS buffer buf
+  auto mma_block = [&](int buf, int kb) {
     const float sw = sw_ptr[kb];
     const uint8_t* wl = w_lds + buf * kTileB + (64 * wn + l32) * kLS + 32 * g;
     const uint8_t* al = a_lds + buf * kTileA + (32 * MT * wm + l32) * kLS + 32 * g;
@@ -198,8 +193,67 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nt][mt][r] = fmaf(part[nt][mt][r], coef[mt], acc[nt][mt][r]);
-    if (kb + 1 < Kb) lstore(buf ^ 1);
+  };
+
+  if constexpr (BM == 128) {
+    gload(0);
+    lstore(0);
     __syncthreads();
+    for (int kb = 0; kb < Kb; ++kb) {
+      const int buf = kb & 1;
+      if (kb + 1 < Kb) gload(kb + 1);
+      mma_block(buf, kb);
+      if (kb + 1 < Kb) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  } else {
+    // 64-token tiles run about one workgroup per CU, with nothing to hide a
+    // step's global loads behind: they are issued two K blocks ahead, into
+    // two register sets (block k in set k % 2).  Step k loads block k + 2
+    // into the set whose block went to LDS at step k - 1, computes block k
+    // and stores block k + 1 (loaded at step k - 1).  The last steps load
+    // and store the final block again rather than branch around the loads.
+    u32x4_t ra2[2][NA], rw2[2][4];
+    float rs2[2];
+    const int last = Kb - 1;
+    auto gload2 = [&](int set, int kb) {
+      const uint8_t* ak = a_tile + kb * kRowB;
+      const uint8_t* wk = w_tile + kb * kRowB;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < NA) ra2[set][i] = *reinterpret_cast<const u32x4_t*>(ak + a_off[i]);
+        rw2[set][i] = *reinterpret_cast<const u32x4_t*>(wk + w_off[i]);
+      }
+      rs2[set] = sa_ptr[kb];
+    };
+    auto lstore2 = [&](int set, int buf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = lrow + 32 * i;
+        if (i < NA) *reinterpret_cast<u32x4_t*>(a_lds + buf * kTileA + row * kLS + lcol) = ra2[set][i];
+        *reinterpret_cast<u32x4_t*>(w_lds + buf * kTileB + row * kLS + lcol) = rw2[set][i];
+      }
+      if (tid < BM) sa_lds[buf][tid] = rs2[set];
+    };
+    auto step = [&](int kb, int set) {
+      gload2(set, min(kb + 2, last));
+      mma_block(set, kb);
+      lstore2(set ^ 1, set ^ 1);
+      __syncthreads();
+    };
+    gload2(0, 0);
+    lstore2(0, 0);
+    gload2(1, min(1, last));
+    __syncthreads();
+    int kb = 0;
+    for (; kb + 2 <= Kb; kb += 2) {
+      step(kb, 0);
+      step(kb + 1, 1);
+    }
+    if (kb < Kb) {
+      mma_block(0, kb);
+      __syncthreads();
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
