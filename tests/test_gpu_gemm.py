@@ -153,6 +153,10 @@ FP8_TILE_SHAPES = [  # (name, N, K, epilogue)
     ("proj", 1152, 1152, O.EPI_BIAS_RESIDUAL),
     ("fc1", 4304, 1152, O.EPI_BIAS_GELU_FP8),
     ("fc2", 1152, 4304, O.EPI_BIAS_RESIDUAL),
+    # odd numbers of 128-deep K blocks (3 and 5): the tails of the 64-token
+    # tiles' loop, which works on K blocks in pairs
+    ("k3_gelu", 4304, 384, O.EPI_BIAS_GELU_FP8),
+    ("k5", 1152, 640, O.EPI_BIAS_RESIDUAL),
 ]
 
 
