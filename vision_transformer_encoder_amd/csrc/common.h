@@ -53,11 +53,25 @@ __device__ __forceinline__ uint32_t e4m3x4_sat(float a, float b, float c, float 
 }
 
 // Block-128 scale: s = amax / 448 and inv = 448 / amax, both correctly
-// rounded fp32 divisions; zero for a (near-)zero block.
+// rounded fp32 divisions; zero for a (near-)zero block.  For amax in
+// [2^-116, 2^126) each quotient is the product with a reciprocal (1/448
+// rounded, or v_rcp_f32 of amax) followed by one correction step with the
+// exact FMA residual, which on gfx950 gives the correctly rounded quotient
+// for every fp32 mantissa at every exponent of that range (compared bit for
+// bit with the IEEE division over all 2^23 mantissas of each exponent); at
+// 2^126 and above v_rcp_f32 is subnormal, so those blocks (and NaN) take the
+// IEEE division itself.
 __device__ __forceinline__ void block_scale(float amax, float& s, float& inv) {
   if (amax < kTinyAmax) {
     s = 0.0f;
     inv = 0.0f;
+  } else if (amax < 0x1p126f) {
+    constexpr float c = 1.0f / kE4M3Max;
+    const float q = amax * c;
+    s = fmaf(fmaf(-q, kE4M3Max, amax), c, q);
+    const float y = __builtin_amdgcn_rcpf(amax);
+    const float p = kE4M3Max * y;
+    inv = fmaf(fmaf(-p, amax, kE4M3Max), y, p);
   } else {
     s = amax / kE4M3Max;
     inv = kE4M3Max / amax;
