@@ -5,7 +5,7 @@
 //  * bf16 (section 4: patch embed and mergers stay bf16) for the patch
 //    embedding (fp32 pixels rounded on load) and the merger MLPs; shapes
 //    with bf16 activations, N % 256 == 0 and K % 192 == 0 (the mergers) go
-//    to the 256-wide tile kernel of gemm_wide.hip.
+//    to the kernel of gemm_wide.hip (256 x 128 tiles, 64 x 64 for small M).
 // Weights are [N, K] row-major (spark_model "layers/vision_encoder.rs":
 // C[M,N] = A[M,K] @ B[N,K]^T + bias), activations [M, K]; both K-contiguous.
 //

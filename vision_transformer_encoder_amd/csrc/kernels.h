@@ -33,8 +33,9 @@ hipError_t launch_bf16_gemm(const void* a, bool a_f32, const uint16_t* w, int M,
                             const uint16_t* bias, const uint16_t* add, int epilogue,
                             uint16_t* out, int64_t ld_out, hipStream_t stream);
 
-// The 256-wide tile bf16 GEMM (gemm_wide.hip) for bf16 A: usable when
-// bf16_gemm_wide_fits(); epilogue 0 (bias) or 1 (bias + GELU).
+// The bf16 GEMM of gemm_wide.hip (256 x 128 tiles, 64 x 64 ones for small
+// M) for bf16 A: usable when bf16_gemm_wide_fits(); epilogue 0 (bias) or 1
+// (bias + GELU).
 bool bf16_gemm_wide_fits(int N, int K, int64_t ld_out, const void* out, const void* bias);
 hipError_t launch_bf16_gemm_wide(const uint16_t* a, const uint16_t* w, int M, int N, int K, const uint16_t* bias,
                                  int epilogue, uint16_t* out, int64_t ld_out, hipStream_t stream);
