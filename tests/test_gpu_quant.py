@@ -121,3 +121,28 @@ def test_quant_zero_scale_threshold(gpu, block_rows):
     assert np.array_equal(host_f64(scales), rs)
     s = host_f64(scales)
     assert np.all(s[0] == 0) and np.all(s[1] > 0) and np.all(s[2] > 0)
+
+
+def test_quant_scales_over_every_bf16_block_max(gpu):
+    """Every positive bf16 value from 2^-116 to the largest finite one as the
+    maximum of a 1 x 128 block (31232 blocks; the other values of a block
+    are bf16 fractions of it, both signs): codes and scales bit-exact against
+    the oracle, i.e. the kernels' amax / 448 and 448 / amax equal the
+    correctly rounded fp32 quotients over the whole range, including the
+    top two binades where the kernels keep the plain division."""
+    biased = np.arange(127 - 116, 255, dtype=np.uint32)          # exponents -116 .. 127
+    mant = np.arange(128, dtype=np.uint32)
+    amax_bits = ((biased[:, None] << 7) | mant[None, :]).ravel().astype(np.uint16)
+    amax = synth.bf16_bits_to_f64(amax_bits)
+    g = np.random.default_rng(21)
+    x = O.bf16(g.uniform(-1.0, 1.0, (amax.size, 128)) * amax[:, None])
+    col = g.integers(0, 128, amax.size)
+    x[np.arange(amax.size), col] = np.where(g.random(amax.size) < 0.5, -amax, amax)
+    assert np.array_equal(np.abs(x).max(axis=1), amax)
+    bits = synth.f32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f64(bits), x)
+    announce(f"vit_quant_fp8_block128 over every bf16 block maximum, {amax.size} blocks")
+    codes, scales = vit.vit_quant_fp8_block128(dev_bf16(bits, gpu), block_rows=1)
+    rc, rs = O.quantize_block128(x, 1)
+    assert np.array_equal(host_f64(scales), rs)
+    assert np.array_equal(host_u8(codes), rc)
