@@ -146,3 +146,30 @@ def test_quant_scales_over_every_bf16_block_max(gpu):
     rc, rs = O.quantize_block128(x, 1)
     assert np.array_equal(host_f64(scales), rs)
     assert np.array_equal(host_u8(codes), rc)
+
+
+@pytest.mark.parametrize("k", [-100, -40, 40, 100, 125])
+def test_layernorm_quant_scaled_gamma(gpu, k):
+    """LayerNorm-quant with gamma and beta scaled by 2^k, so that the fp32
+    block maxima (every mantissa, not only bf16 ones) lie near 2^(k+2): the
+    quantiser on the GPU's own pre-quant values is bit-exact against the
+    oracle's at each scale, up to the top binade (k = 125), where the
+    kernels keep the plain division."""
+    M = 1024
+    x = synth.normal_bf16(0, "x", 500 + k, (M, 1152))
+    gf = O.bf16(np.ldexp(1.0 + 0.02 * np.random.default_rng(k + 400).standard_normal(1152), k))
+    bf = O.bf16(np.ldexp(0.01 * np.random.default_rng(k + 600).standard_normal(1152), k))
+    g = synth.f32_to_bf16_bits(gf.astype(np.float32))
+    b = synth.f32_to_bf16_bits(bf.astype(np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f64(g), gf) and np.array_equal(synth.bf16_bits_to_f64(b), bf)
+    announce(f"vit_layernorm_quant_fp8 gamma x 2^{k}")
+    codes, scales, pre = vit.vit_layernorm_quant_fp8(dev_bf16(x, gpu), dev_bf16(g, gpu), dev_bf16(b, gpu), 1e-6,
+                                                     prequant=True)
+    pre_h = host_f64(pre)
+    ref = O.layernorm(synth.bf16_bits_to_f64(x), gf, bf)
+    assert_close(pre_h, ref, 1e-5, 0.99999999, f"LN prequant, gamma x 2^{k}")
+    rc, rs = O.quantize_block128(pre_h, 1)
+    assert np.array_equal(host_f64(scales), rs)
+    assert np.array_equal(host_u8(codes), rc)
+    amax = np.abs(pre_h).reshape(M, 9, 128).max(axis=2)
+    assert amax.min() >= 2.0 ** (k - 1) and amax.max() < 2.0 ** (k + 4)
