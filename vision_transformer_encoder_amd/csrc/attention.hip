@@ -670,6 +670,32 @@ __global__ __launch_bounds__(2 * kBQ) void attention_combine_kernel(AttnParams a
       l = fmaf(w1, l1, fmaf(w0, l0, 0.0f));
 #pragma unroll
       for (int i = 0; i < kHalf; ++i) o[i] = fmaf(w1, o1[i], fmaf(w0, o0[i], 0.0f));
+    } else if (lg - g0 < 4) {
+      // three or four segments (short ranges, small windows): the same,
+      // with the values of a fourth segment loaded from the last one again
+      // and not used
+      constexpr int kS = 4;
+      const int ns = lg - g0 + 1;
+      float mv[kS], lv[kS], ov[kS][kHalf];
+#pragma unroll
+      for (int j = 0; j < kS; ++j) {
+        const float* sl = slot_of(min(g0 + j, lg));
+        mv[j] = sl[(kHD + 1) * kBQ + qi];
+        lv[j] = sl[kHD * kBQ + qi];
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) ov[j][i] = sl[(half * kHalf + i) * kBQ + qi];
+      }
+#pragma unroll
+      for (int j = 0; j < kS; ++j) m = j < ns ? fmaxf(m, mv[j]) : m;
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) o[i] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kS; ++j) {
+        const float w = __builtin_amdgcn_exp2f(mv[j] - m);
+        l = j < ns ? fmaf(w, lv[j], l) : l;
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) o[i] = j < ns ? fmaf(w, ov[j][i], o[i]) : o[i];
+      }
     } else {
       for (int gg = g0; gg <= lg; ++gg) m = fmaxf(m, slot_of(gg)[(kHD + 1) * kBQ + qi]);
 #pragma unroll
