@@ -26,10 +26,11 @@
  *  - The caller owns all memory it passes.  No entry point allocates, and
  *    the library is safe to call from several threads.  Its process-wide
  *    state: a cache of each device's compute-unit count (atomic, written on
- *    the first attention call on that device; every later call reads the
- *    same value) and, for vit_attention_noalloc only, one scratch array per
- *    device held in the code object, whose address is taken on the first
- *    such call on that device (see that entry point).
+ *    the first attention or GEMM launch on that device, which size their
+ *    grids from it; every later call reads the same value) and, for
+ *    vit_attention_noalloc only, one scratch array per device held in the
+ *    code object, whose address is taken on the first such call on that
+ *    device (see that entry point).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *    and runs asynchronously; no call synchronises with the host.
  *    Buffers must stay valid until that work has finished.
